@@ -1,0 +1,12 @@
+"""CPU oracle for LongNet dilated attention (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package.
+"""
+from .dilated import (backward, brute_force_forward, check_patterns, combine, forward,
+                      forward_rows, multiplicity, pair_count, row_map, segment_attention,
+                      useful_flops)
+
+__all__ = ["backward", "brute_force_forward", "check_patterns", "combine", "forward",
+           "forward_rows", "multiplicity", "pair_count", "row_map", "segment_attention",
+           "useful_flops"]
