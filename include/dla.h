@@ -1,0 +1,147 @@
+/*
+ * dla.h - C ABI of libdla: LongNet dilated attention on AMD MI355X (gfx950).
+ *
+ * Sources (web pages about LongNet, arXiv 2307.02486), cited below as:
+ *   [G] the gptget.net summary page of arXiv 2307.02486; sections 方法论
+ *       (method), 方法详解 (method details), 实验设计 (experiment design),
+ *       原文摘要 (the English abstract);
+ *   [D] the darcstar.tech research page "LongNet: Scaling Transformers to
+ *       1,000,000,000 Tokens", the DarcStar commentary.
+ *
+ * The operator ([G] 方法论, 方法详解): for each pattern (w, r) the sequence is
+ * split into segments of w rows; in each segment every r-th row is kept,
+ * starting at row (h mod r) for head h, for Q, K and V alike; dense softmax
+ * attention runs inside each sparsified segment.  Patterns are merged with
+ * weights exp(LSE_p - LSE), LSE = log sum_p exp(LSE_p), so the softmax
+ * denominator they share stays exact ([D] commentary).  With `causal`, a row
+ * attends only to rows at or before it inside its sparsified segment.  A row
+ * that no pattern keeps gets O = 0 and LSE = -inf.  The method is a drop-in
+ * replacement for standard attention ([G] 原文摘要): one pattern (N, 1) is
+ * full softmax attention.
+ *
+ * Conventions for every entry point:
+ *   - Tensors q, k, v, o, dout, dq, dk, dv are device pointers to
+ *     [B, N, H, D] tensors with element strides (stride_b, stride_n,
+ *     stride_h) and a contiguous last dimension.  D must be 64.  Element type
+ *     is shape->dtype (fp32 or bf16; bf16 paths compute in bf16 with fp32
+ *     accumulation).  lse is a device pointer to a contiguous fp32 [B, H, N]
+ *     tensor holding natural-log log-sum-exp values.
+ *   - All device pointers and strides*element size must be 16-byte aligned.
+ *     An empty problem (B == 0 or H == 0) reads and writes nothing, so its
+ *     pointers are not checked and may be null.
+ *   - The caller owns every buffer, including the workspace; the library
+ *     allocates and frees nothing, keeps no device state and never
+ *     synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and returns before it runs.
+ *   - Descriptors are caller-owned host memory read only during the call.
+ *   - Return value: DLA_OK or a negative DLA_E_* code.  All validation runs on
+ *     the host before anything is enqueued; a failed call enqueues nothing.
+ *     dla_last_error() returns the calling thread's message for its last
+ *     failed call.
+ */
+#ifndef DLA_H_
+#define DLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLA_MAX_PATTERNS 16
+#define DLA_HEAD_DIM 64
+
+#define DLA_OK 0
+#define DLA_E_INVALID (-1)      /* null/misaligned pointer, bad w or r, bad scale or count */
+#define DLA_E_UNSUPPORTED (-2)  /* D != 64, N % w != 0, w % r != 0, w > N, unknown dtype */
+#define DLA_E_WORKSPACE (-3)    /* workspace smaller than dla_plan_check reports */
+#define DLA_E_HIP (-4)          /* the HIP runtime refused a launch */
+
+typedef enum { DLA_F32 = 0, DLA_BF16 = 1 } dla_dtype;
+
+/* One dilation pattern: segment length w, dilation rate r ([G] 方法论). */
+typedef struct {
+  int32_t w;
+  int32_t r;
+} dla_pattern;
+
+/* The operator: 1..16 patterns (host memory), a causal flag (0/1) and the
+ * softmax scale applied to q.k (finite, > 0; 1/sqrt(D) for standard use). */
+typedef struct {
+  int32_t num_patterns;
+  const dla_pattern* patterns;
+  int32_t causal;
+  float scale;
+} dla_desc;
+
+/* Problem shape and element strides of q/k/v/o (and the gradients). */
+typedef struct {
+  int64_t B, N, H, D;
+  int32_t dtype; /* dla_dtype */
+  int64_t stride_b, stride_n, stride_h;
+} dla_shape;
+
+/*
+ * Validate a descriptor and shape on the host and report the workspace bytes
+ * dla_forward and dla_backward need (either out-pointer may be NULL).  Needs
+ * no GPU.  B == 0 or H == 0 is a valid empty problem.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
+ */
+int dla_plan_check(const dla_desc* desc, const dla_shape* shape, size_t* ws_fwd_bytes,
+                   size_t* ws_bwd_bytes);
+
+/*
+ * Forward pass ([G] 方法论; [D] commentary).  Writes o ([B,N,H,D], input
+ * dtype) and lse ([B,H,N] fp32).  ws must hold at least the forward workspace
+ * size of dla_plan_check (it stores the per-pattern partial results of all
+ * patterns but the one that keeps the most rows).
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_WORKSPACE, DLA_E_HIP.
+ */
+int dla_forward(const dla_desc* desc, const dla_shape* shape, const void* q, const void* k,
+                const void* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward pass: gradients of sum(dout * o) with respect to q, k and v, where
+ * (o, lse) are the outputs of dla_forward for the same q, k, v, desc and
+ * shape.  The merge weights are differentiated through (the combined output
+ * is one softmax over the union of each row's keys), so each pattern uses the
+ * combined lse and D = rowsum(dout * o).  dq, dk, dv have the input dtype and
+ * the strides of `shape`; they are accumulated over patterns in fp32 in the
+ * workspace and rounded once.  Deterministic: no atomics.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_WORKSPACE, DLA_E_HIP.
+ */
+int dla_backward(const dla_desc* desc, const dla_shape* shape, const void* q, const void* k,
+                 const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                 void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Index map of one pattern ([G] 方法论: segment, dilation, head offset):
+ * out[h * (N / r) + s * (w / r) + a] = s * w + (h mod r) + a * r, the original
+ * row of sparse row a of segment s, for every head h < H.  out is a device
+ * int32 buffer of H * (N / r) entries.  This is the address generator every
+ * kernel uses, exposed so that it can be compared bit for bit.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_HIP.
+ */
+int dla_row_map(const dla_desc* desc, int64_t N, int32_t H, int32_t pattern, int32_t* out,
+                void* stream);
+
+/*
+ * Number of (query, key) pairs the operator evaluates, summed over batch,
+ * heads and patterns: B*H*sum_p (N/w_p) * (L_p(L_p+1)/2 if causal else L_p^2)
+ * with L_p = w_p / r_p.  Linear in N for fixed L_p ([G] 方法论).  Host only.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
+ */
+int dla_pair_count(const dla_desc* desc, const dla_shape* shape, int64_t* pairs);
+
+/* Static text for an error code. */
+const char* dla_strerror(int code);
+
+/* The calling thread's message for its last failed call ("" if none). */
+const char* dla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLA_H_ */

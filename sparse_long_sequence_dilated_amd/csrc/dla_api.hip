@@ -1,0 +1,130 @@
+// C ABI entry points of libdla that enqueue GPU work (see include/dla.h).
+// Every check runs on the host before the first launch; a failing call
+// enqueues nothing.
+#include <stdint.h>
+
+#include "dla_kernels.h"
+
+namespace dla {
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(DLA_E_INVALID, "%s is null", name);
+  if (!aligned16(p)) return fail(DLA_E_INVALID, "%s is not 16-byte aligned", name);
+  return DLA_OK;
+}
+
+static int hip_fail(hipError_t e, const char* what) {
+  return fail(DLA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static void fill_fwd_args(const Plan& pl, AttnFwdArgs* a) {
+  a->sb = pl.sb;
+  a->sn = pl.sn;
+  a->sh = pl.sh;
+  a->B = pl.B;
+  a->N = pl.N;
+  a->H = pl.H;
+  a->P = pl.P;
+  a->prim = pl.prim;
+  a->causal = pl.causal;
+  a->scale = pl.scale;
+  a->scale_log2 = pl.scale * 1.4426950408889634f;
+  for (int i = 0; i < pl.P; ++i) {
+    a->w[i] = pl.w[i];
+    a->r[i] = pl.r[i];
+    a->L[i] = pl.L[i];
+    a->nseg[i] = pl.nseg[i];
+  }
+}
+
+}  // namespace dla
+
+using namespace dla;
+
+extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const void* q,
+                           const void* k, const void* v, void* o, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl);
+  if (rc) return rc;
+  if (pl.empty) return DLA_OK;  // nothing is read or written; pointers may be null
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")))
+    return rc;
+  if (ws_bytes < pl.ws_fwd)
+    return fail(DLA_E_WORKSPACE, "forward workspace needs %zu bytes, got %zu", pl.ws_fwd, ws_bytes);
+  if (pl.ws_fwd && (rc = check_ptr(ws, "workspace"))) return rc;
+
+  AttnFwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  fill_fwd_args(pl, &a);
+  for (int i = 0; i < pl.P; ++i) {
+    if (i == pl.prim) continue;
+    a.part_o[i] = (char*)ws + pl.part_o_off[i];
+    a.part_lse[i] = (float*)((char*)ws + pl.part_lse_off[i]);
+  }
+  make_schedule(pl, pl.dtype == DLA_BF16 ? 256 : 64, &a.sched);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = pl.dtype == DLA_BF16 ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_f32(a, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (pl.need_combine) {
+    CombineArgs cb{};
+    cb.o = o;
+    cb.lse = lse;
+    for (int i = 0; i < pl.P; ++i) {
+      cb.part_o[i] = a.part_o[i];
+      cb.part_lse[i] = a.part_lse[i];
+      cb.r[i] = pl.r[i];
+    }
+    cb.sb = pl.sb;
+    cb.sn = pl.sn;
+    cb.sh = pl.sh;
+    cb.B = pl.B;
+    cb.N = pl.N;
+    cb.H = pl.H;
+    cb.P = pl.P;
+    cb.prim = pl.prim;
+    e = launch_combine(cb, pl.dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return DLA_OK;
+}
+
+extern "C" int dla_row_map(const dla_desc* desc, int64_t N, int32_t H, int32_t pattern,
+                           int32_t* out, void* stream) {
+  clear_error();
+  dla_shape sh{};
+  sh.B = 1;
+  sh.N = N;
+  sh.H = H;
+  sh.D = kD;
+  sh.dtype = DLA_BF16;
+  sh.stride_h = kD;
+  sh.stride_n = (H > 0 ? H : 1) * kD;
+  sh.stride_b = N * sh.stride_n;
+  Plan pl;
+  int rc = make_plan(desc, &sh, &pl);
+  if (rc) return rc;
+  if (pattern < 0 || pattern >= pl.P)
+    return fail(DLA_E_INVALID, "pattern index %d outside 0..%d", pattern, pl.P - 1);
+  if (!out) return fail(DLA_E_INVALID, "out is null");
+  if ((uintptr_t)out & 3u) return fail(DLA_E_INVALID, "out is not 4-byte aligned");
+  if (H == 0) return DLA_OK;
+  RowMapArgs a{};
+  a.out = out;
+  a.N = N;
+  a.H = H;
+  a.w = pl.w[pattern];
+  a.r = pl.r[pattern];
+  a.L = pl.L[pattern];
+  hipError_t e = launch_row_map(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "row map launch");
+  return DLA_OK;
+}

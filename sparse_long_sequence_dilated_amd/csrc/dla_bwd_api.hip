@@ -1,0 +1,113 @@
+// C ABI entry point of the backward pass (see include/dla.h).
+//
+// Launch sequence on the caller's stream: one preprocessing pass (D =
+// rowsum(dO*O), zero gradients for rows no pattern keeps), then one launch
+// per pattern.  Patterns other than the one keeping the most rows go first,
+// that one last; each launch's epilogue knows, per row, whether an earlier
+// or a later pattern keeps it, so fp32 accumulation only happens for rows
+// kept by several patterns and every gradient is rounded exactly once.
+#include <stdint.h>
+
+#include "dla_kernels.h"
+
+using namespace dla;
+
+static int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(DLA_E_INVALID, "%s is null", name);
+  if ((uintptr_t)p & 15u) return fail(DLA_E_INVALID, "%s is not 16-byte aligned", name);
+  return DLA_OK;
+}
+
+extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const void* q,
+                            const void* k, const void* v, const void* o, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl);
+  if (rc) return rc;
+  if (pl.empty) return DLA_OK;  // nothing is read or written; pointers may be null
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")) || (rc = check_ptr(dout, "dout")) ||
+      (rc = check_ptr(dq, "dq")) || (rc = check_ptr(dk, "dk")) || (rc = check_ptr(dv, "dv")))
+    return rc;
+  if (ws_bytes < pl.ws_bwd)
+    return fail(DLA_E_WORKSPACE, "backward workspace needs %zu bytes, got %zu", pl.ws_bwd, ws_bytes);
+  if ((rc = check_ptr(ws, "workspace"))) return rc;
+  if (pl.dtype != DLA_BF16)
+    return fail(DLA_E_UNSUPPORTED, "the backward pass is implemented for bf16 tensors");
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  float* delta = (float*)(wsb + pl.delta_off);
+
+  BwdPrepArgs pa{};
+  pa.o = o;
+  pa.dout = dout;
+  pa.delta = delta;
+  pa.dq = dq;
+  pa.dk = dk;
+  pa.dv = dv;
+  pa.sb = pl.sb;
+  pa.sn = pl.sn;
+  pa.sh = pl.sh;
+  pa.B = pl.B;
+  pa.N = pl.N;
+  pa.H = pl.H;
+  pa.P = pl.P;
+  for (int i = 0; i < pl.P; ++i) pa.r_all[i] = pl.r[i];
+  pa.zero_uncovered = pl.r[pl.prim] != 1;
+  hipError_t e = launch_bwd_prep(pa, pl.dtype, st);
+  if (e != hipSuccess) return fail(DLA_E_HIP, "backward preprocessing launch: %s", hipGetErrorString(e));
+
+  int order[kMaxP], n = 0;
+  for (int i = 0; i < pl.P; ++i)
+    if (i != pl.prim) order[n++] = i;
+  order[n++] = pl.prim;
+
+  AttnBwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq_acc = (float*)(wsb + pl.dq_off);
+  a.dk_acc = (float*)(wsb + pl.dk_off);
+  a.dv_acc = (float*)(wsb + pl.dv_off);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.sb = pl.sb;
+  a.sn = pl.sn;
+  a.sh = pl.sh;
+  a.B = pl.B;
+  a.N = pl.N;
+  a.H = pl.H;
+  a.causal = pl.causal;
+  a.scale = pl.scale;
+  a.scale_log2 = pl.scale * 1.4426950408889634f;
+  a.P = pl.P;
+  for (int i = 0; i < pl.P; ++i) {
+    a.r_all[i] = pl.r[i];
+    a.rank[order[i]] = i;
+  }
+  for (int i = 0; i < pl.P; ++i) {
+    const int p = order[i];
+    a.p = p;
+    a.w = pl.w[p];
+    a.r = pl.r[p];
+    a.L = pl.L[p];
+    a.nseg = pl.nseg[p];
+    Plan one = pl;  // one-pattern view for the unit schedule
+    one.P = 1;
+    one.w[0] = pl.w[p];
+    one.r[0] = pl.r[p];
+    one.L[0] = pl.L[p];
+    one.nseg[0] = pl.nseg[p];
+    make_schedule(one, 128, &a.sched_kv);
+    make_schedule(one, 128, &a.sched_q);
+    e = launch_attn_bwd_bf16(a, st);
+    if (e != hipSuccess) return fail(DLA_E_HIP, "backward launch: %s", hipGetErrorString(e));
+  }
+  return DLA_OK;
+}

@@ -1,0 +1,96 @@
+// Kernel argument blocks and launchers of libdla (host and device side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "dla_plan.h"
+
+namespace dla {
+
+// Attention pass over all patterns (forward), one launch.
+struct AttnFwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* part_o[kMaxP];     // per-pattern partial O_p [B,H,N/r,D] (unused for prim)
+  float* part_lse[kMaxP];  // per-pattern partial LSE_p [B,H,N/r]
+  int64_t sb, sn, sh;
+  int64_t B, N, H;
+  int P, prim, causal;
+  float scale;             // softmax scale
+  float scale_log2;        // scale * log2(e)
+  int w[kMaxP], r[kMaxP], L[kMaxP];
+  int64_t nseg[kMaxP];
+  Schedule sched;
+};
+
+// Merge of the per-pattern results into o/lse.
+struct CombineArgs {
+  void* o;
+  float* lse;
+  const void* part_o[kMaxP];
+  const float* part_lse[kMaxP];
+  int64_t sb, sn, sh;
+  int64_t B, N, H;
+  int P, prim;
+  int r[kMaxP];
+};
+
+struct RowMapArgs {
+  int32_t* out;
+  int64_t N;
+  int H, w, r, L;
+};
+
+// Backward of one pattern: dK/dV units (one per key tile) and dQ units (one
+// per query tile) in one launch; both read the combined LSE and D.
+struct AttnBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;        // combined LSE [B,H,N]
+  const float* delta;      // D = rowsum(dO*O) [B,H,N]
+  float* dq_acc;           // fp32 [B,N,H,D] accumulators (contiguous)
+  float* dk_acc;
+  float* dv_acc;
+  void* dq;                // outputs, input dtype, strides sb/sn/sh
+  void* dk;
+  void* dv;
+  int64_t sb, sn, sh;
+  int64_t B, N, H;
+  int causal;
+  float scale, scale_log2;
+  int p, w, r, L;          // the pattern of this launch
+  int64_t nseg;
+  int P;
+  int r_all[kMaxP];        // dilation rate of every pattern
+  int rank[kMaxP];         // processing order of every pattern
+  Schedule sched_kv;       // dK/dV units (key tiles)
+  Schedule sched_q;        // dQ units (query tiles)
+};
+
+struct BwdPrepArgs {
+  const void* o;
+  const void* dout;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t sb, sn, sh;
+  int64_t B, N, H;
+  int P;
+  int r_all[kMaxP];
+  int zero_uncovered;      // write zero gradients for rows no pattern keeps
+};
+
+hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_row_map(const RowMapArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_prep(const BwdPrepArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace dla

@@ -1,0 +1,184 @@
+// Host planner of libdla (see dla_plan.h).  No HIP here: this file also
+// builds with g++ alone for CPU tests under the address and UB sanitizers.
+#include "dla_plan.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+namespace dla {
+
+static thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan) {
+  if (!desc || !shape || !plan) return fail(DLA_E_INVALID, "null descriptor or shape");
+  Plan& p = *plan;
+  memset(&p, 0, sizeof(p));
+  if (desc->num_patterns < 1 || desc->num_patterns > kMaxP)
+    return fail(DLA_E_INVALID, "num_patterns=%d outside 1..%d", desc->num_patterns, kMaxP);
+  if (!desc->patterns) return fail(DLA_E_INVALID, "null pattern array");
+  if (desc->causal != 0 && desc->causal != 1)
+    return fail(DLA_E_INVALID, "causal=%d is not 0 or 1", desc->causal);
+  if (!isfinite(desc->scale) || !(desc->scale > 0.0f))
+    return fail(DLA_E_INVALID, "scale must be finite and > 0");
+  if (shape->dtype != DLA_F32 && shape->dtype != DLA_BF16)
+    return fail(DLA_E_UNSUPPORTED, "dtype=%d is neither DLA_F32 nor DLA_BF16", shape->dtype);
+  if (shape->D != kD) return fail(DLA_E_UNSUPPORTED, "head dim D=%lld, only 64 is supported",
+                                  (long long)shape->D);
+  if (shape->B < 0 || shape->H < 0 || shape->N < 1)
+    return fail(DLA_E_INVALID, "bad sizes B=%lld N=%lld H=%lld", (long long)shape->B,
+                (long long)shape->N, (long long)shape->H);
+  if (shape->N > (int64_t)INT32_MAX || shape->H > 65535)
+    return fail(DLA_E_UNSUPPORTED, "N must be < 2^31 and H <= 65535");
+  if (shape->stride_b <= 0 || shape->stride_n <= 0 || shape->stride_h <= 0)
+    return fail(DLA_E_INVALID, "strides must be positive");
+  if (shape->stride_b % 8 || shape->stride_n % 8 || shape->stride_h % 8)
+    return fail(DLA_E_INVALID, "strides must be multiples of 8 elements (16-byte rows)");
+
+  p.B = shape->B;
+  p.N = shape->N;
+  p.H = shape->H;
+  p.dtype = shape->dtype;
+  p.esize = shape->dtype == DLA_F32 ? 4 : 2;
+  p.sb = shape->stride_b;
+  p.sn = shape->stride_n;
+  p.sh = shape->stride_h;
+  p.P = desc->num_patterns;
+  p.causal = desc->causal;
+  p.scale = desc->scale;
+  p.empty = (p.B == 0 || p.H == 0);
+
+  for (int i = 0; i < p.P; ++i) {
+    const int w = desc->patterns[i].w, r = desc->patterns[i].r;
+    if (w < 1 || r < 1) return fail(DLA_E_INVALID, "pattern %d: w=%d r=%d must be >= 1", i, w, r);
+    if (w % r) return fail(DLA_E_UNSUPPORTED, "pattern %d: r=%d does not divide w=%d", i, r, w);
+    if (w > p.N) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d exceeds N=%lld", i, w,
+                             (long long)p.N);
+    if (p.N % w) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d does not divide N=%lld", i, w,
+                             (long long)p.N);
+    p.w[i] = w;
+    p.r[i] = r;
+    p.L[i] = w / r;
+    p.nseg[i] = p.N / w;
+  }
+
+  // The pattern that keeps the most rows (smallest r, first on ties) writes
+  // o/lse directly; the others leave partial results for the merge pass.
+  p.prim = 0;
+  for (int i = 1; i < p.P; ++i)
+    if (p.r[i] < p.r[p.prim]) p.prim = i;
+  p.need_combine = !(p.P == 1 && p.r[0] == 1);
+
+  size_t off = 0;
+  for (int i = 0; i < p.P; ++i) {
+    p.part_o_off[i] = p.part_lse_off[i] = (size_t)-1;
+    if (i == p.prim) continue;
+    const size_t rows = (size_t)p.B * p.H * (p.N / p.r[i]);
+    p.part_o_off[i] = off;
+    off = align_up(off + rows * kD * p.esize, 256);
+    p.part_lse_off[i] = off;
+    off = align_up(off + rows * sizeof(float), 256);
+  }
+  p.ws_fwd = off;
+
+  const size_t rows_all = (size_t)p.B * p.N * p.H;
+  off = 0;
+  p.delta_off = off;
+  off = align_up(off + rows_all * sizeof(float), 256);
+  p.dq_off = off;
+  off = align_up(off + rows_all * kD * sizeof(float), 256);
+  p.dk_off = off;
+  off = align_up(off + rows_all * kD * sizeof(float), 256);
+  p.dv_off = off;
+  off = align_up(off + rows_all * kD * sizeof(float), 256);
+  p.ws_bwd = off;
+
+  int64_t pairs = 0;
+  for (int i = 0; i < p.P; ++i) {
+    const int64_t L = p.L[i];
+    pairs += p.nseg[i] * (p.causal ? L * (L + 1) / 2 : L * L);
+  }
+  p.pairs = pairs * p.B * p.H;
+  return DLA_OK;
+}
+
+void make_schedule(const Plan& p, int tile_rows, Schedule* s) {
+  memset(s, 0, sizeof(*s));
+  int ntile[kMaxP];
+  for (int i = 0; i < p.P; ++i) {
+    ntile[i] = (p.L[i] + tile_rows - 1) / tile_rows;
+    s->order[i] = i;
+  }
+  std::stable_sort(s->order, s->order + p.P,
+                   [&](int a, int b) { return ntile[a] > ntile[b]; });
+  s->cum[0] = 0;
+  for (int i = 0; i < p.P; ++i) s->cum[i + 1] = s->cum[i] + p.B * p.H * p.nseg[s->order[i]];
+  int64_t start = 0;
+  int nb = 0;
+  for (int i = 0; i < p.P; ++i) {
+    const int hi = ntile[s->order[i]];
+    const int lo = (i + 1 < p.P) ? ntile[s->order[i + 1]] : 0;
+    if (hi == lo) continue;
+    s->band_hi[nb] = hi;
+    s->band_npat[nb] = i + 1;
+    s->band_start[nb] = start;
+    start += (int64_t)(hi - lo) * s->cum[i + 1];
+    ++nb;
+  }
+  s->band_start[nb] = start;
+  s->nband = nb;
+  s->total = start;
+}
+
+}  // namespace dla
+
+extern "C" {
+
+int dla_plan_check(const dla_desc* desc, const dla_shape* shape, size_t* ws_fwd_bytes,
+                   size_t* ws_bwd_bytes) {
+  dla::Plan p;
+  const int rc = dla::make_plan(desc, shape, &p);
+  if (rc != DLA_OK) return rc;
+  if (ws_fwd_bytes) *ws_fwd_bytes = p.ws_fwd;
+  if (ws_bwd_bytes) *ws_bwd_bytes = p.ws_bwd;
+  return DLA_OK;
+}
+
+int dla_pair_count(const dla_desc* desc, const dla_shape* shape, int64_t* pairs) {
+  dla::Plan p;
+  const int rc = dla::make_plan(desc, shape, &p);
+  if (rc != DLA_OK) return rc;
+  if (!pairs) return dla::fail(DLA_E_INVALID, "null output pointer");
+  *pairs = p.pairs;
+  return DLA_OK;
+}
+
+const char* dla_strerror(int code) {
+  switch (code) {
+    case DLA_OK: return "success";
+    case DLA_E_INVALID: return "invalid argument";
+    case DLA_E_UNSUPPORTED: return "unsupported configuration";
+    case DLA_E_WORKSPACE: return "workspace too small";
+    case DLA_E_HIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+const char* dla_last_error(void) { return dla::g_err; }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Host planner of libdla: validation, workspace layout and the work-unit
+// schedule shared by all launches.  Pure C++ (no HIP), so it is built and
+// tested on the CPU as well.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dla.h"
+
+namespace dla {
+
+constexpr int kMaxP = DLA_MAX_PATTERNS;
+constexpr int kD = DLA_HEAD_DIM;
+
+// Longest-first decode of a flat work-unit index into (pattern, batch, head,
+// segment, tile).  A unit is one tile of rows of one sparsified segment.
+// Under a causal mask the work of a tile grows with its index, so units are
+// ordered by tile index, highest first, with all patterns interleaved at each
+// tile level; inside a level the order is pattern, batch, head, segment.
+struct Schedule {
+  int nband;                    // bands of tile levels with the same active patterns
+  int order[kMaxP];             // patterns sorted by tile count, descending
+  int64_t cum[kMaxP + 1];       // prefix sums of B*H*nseg over `order`
+  int band_hi[kMaxP];           // band covers tile levels [band_lo, band_hi), high first
+  int band_npat[kMaxP];         // patterns active in the band (a prefix of `order`)
+  int64_t band_start[kMaxP + 1];
+  int64_t total;                // number of units
+};
+
+struct Plan {
+  int64_t B, N, H;
+  int dtype;                    // dla_dtype
+  int esize;                    // bytes per element of q/k/v/o
+  int64_t sb, sn, sh;           // element strides of [B, N, H, D] tensors
+  int P;
+  int causal;
+  float scale;
+  int w[kMaxP], r[kMaxP], L[kMaxP];
+  int64_t nseg[kMaxP];
+  int prim;                     // pattern whose result goes straight to o/lse
+  bool need_combine;            // a merge pass is needed after the attention pass
+  bool empty;                   // B == 0 or H == 0: nothing to do
+  // forward workspace: per-pattern partial O_p [B,H,N/r,D] and LSE_p [B,H,N/r]
+  size_t part_o_off[kMaxP];
+  size_t part_lse_off[kMaxP];
+  size_t ws_fwd;
+  // backward workspace: D = rowsum(dO*O) [B,H,N] fp32, fp32 accumulators [B,N,H,D]
+  size_t delta_off, dq_off, dk_off, dv_off;
+  size_t ws_bwd;
+  int64_t pairs;
+};
+
+// Validate and fill `plan`.  Returns DLA_OK or an error code; the message is
+// recorded for dla_last_error().
+int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan);
+
+// Fill `s` for tiles of `tile_rows` sparse rows per unit.
+void make_schedule(const Plan& plan, int tile_rows, Schedule* s);
+
+// Record a formatted message for dla_last_error() and return `code`.
+int fail(int code, const char* fmt, ...);
+void clear_error();
+
+}  // namespace dla

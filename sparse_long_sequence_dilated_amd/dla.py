@@ -1,0 +1,222 @@
+"""ctypes binding of libdla (include/dla.h): argument marshalling only.
+
+PyTorch provides device memory and the current HIP stream; every step of the
+computation runs in libdla's kernels.  The library must have been built
+(``python -m sparse_long_sequence_dilated_amd.build``); loading fails loudly
+otherwise, and there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdla.so")
+
+DLA_OK = 0
+DLA_E_INVALID = -1
+DLA_E_UNSUPPORTED = -2
+DLA_E_WORKSPACE = -3
+DLA_E_HIP = -4
+DLA_F32 = 0
+DLA_BF16 = 1
+MAX_PATTERNS = 16
+HEAD_DIM = 64
+
+EXPORTS = ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
+           "dla_strerror", "dla_last_error")
+
+
+class DlaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libdla error {code}: {msg}")
+        self.code = code
+
+
+class Pattern(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_int32), ("r", ctypes.c_int32)]
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("num_patterns", ctypes.c_int32), ("patterns", ctypes.POINTER(Pattern)),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("N", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("dtype", ctypes.c_int32), ("stride_b", ctypes.c_int64),
+                ("stride_n", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdla.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_long_sequence_dilated_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    pd, ps = ctypes.POINTER(Desc), ctypes.POINTER(Shape)
+    L.dla_plan_check.argtypes = [pd, ps, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.dla_forward.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dla_backward.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dla_row_map.argtypes = [pd, i64, i32, i32, vp, vp]
+    L.dla_pair_count.argtypes = [pd, ps, ctypes.POINTER(i64)]
+    L.dla_strerror.argtypes = [ctypes.c_int]
+    L.dla_strerror.restype = ctypes.c_char_p
+    L.dla_last_error.argtypes = []
+    L.dla_last_error.restype = ctypes.c_char_p
+    for name in ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != DLA_OK:
+        raise DlaError(rc, lib().dla_last_error().decode() or lib().dla_strerror(rc).decode())
+
+
+def make_desc(patterns, causal: bool, scale: float):
+    arr = (Pattern * max(1, len(patterns)))(*[Pattern(int(w), int(r)) for w, r in patterns])
+    d = Desc(len(patterns), ctypes.cast(arr, ctypes.POINTER(Pattern)), int(bool(causal)),
+             float(scale))
+    d._keep = arr  # keep the pattern array alive with the descriptor
+    return d
+
+
+def make_shape(B, N, H, D, dtype, strides=None):
+    if strides is None:
+        strides = (N * H * D, H * D, D)
+    return Shape(B, N, H, D, dtype, *strides)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return DLA_F32
+    if t.dtype == torch.bfloat16:
+        return DLA_BF16
+    raise DlaError(DLA_E_UNSUPPORTED, f"dtype {t.dtype} is neither float32 nor bfloat16")
+
+
+def _shape_of(t):
+    if t.dim() != 4:
+        raise DlaError(DLA_E_INVALID, "tensors must be [B, N, H, D]")
+    if t.stride(3) != 1:
+        raise DlaError(DLA_E_INVALID, "the last dimension must be contiguous")
+    B, N, H, D = t.shape
+    return make_shape(B, N, H, D, _dtype_code(t), (t.stride(0), t.stride(1), t.stride(2)))
+
+
+def _same_layout(ref, *ts):
+    for t in ts:
+        if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
+            raise DlaError(DLA_E_INVALID, "q, k, v, o (and gradients) need one shape, stride and dtype")
+        if t.device != ref.device:
+            raise DlaError(DLA_E_INVALID, "all tensors must be on one device")
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def plan_check(patterns, causal, scale, B, N, H, D=HEAD_DIM, dtype=DLA_BF16, strides=None):
+    """Return (ws_fwd_bytes, ws_bwd_bytes); raises DlaError on an invalid problem."""
+    d = make_desc(patterns, causal, scale)
+    s = make_shape(B, N, H, D, dtype, strides)
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().dla_plan_check(ctypes.byref(d), ctypes.byref(s), ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+def plan_check_code(patterns, causal, scale, B, N, H, D=HEAD_DIM, dtype=DLA_BF16, strides=None):
+    """Raw return code of dla_plan_check (for error-path tests)."""
+    d = make_desc(patterns, causal, scale)
+    s = make_shape(B, N, H, D, dtype, strides)
+    return lib().dla_plan_check(ctypes.byref(d), ctypes.byref(s), None, None)
+
+
+def pair_count(patterns, causal, B, N, H, D=HEAD_DIM, dtype=DLA_BF16):
+    d = make_desc(patterns, causal, 1.0)
+    s = make_shape(B, N, H, D, dtype)
+    out = ctypes.c_int64(0)
+    _check(lib().dla_pair_count(ctypes.byref(d), ctypes.byref(s), ctypes.byref(out)))
+    return out.value
+
+
+def default_scale(D=HEAD_DIM):
+    return 1.0 / math.sqrt(D)
+
+
+def forward(q, k, v, patterns, causal=True, scale=None, out=None, lse=None, workspace=None,
+            stream=None):
+    """Dilated attention forward on the GPU; returns (o, lse).
+
+    q, k, v: [B, N, H, 64] float32 or bfloat16 CUDA tensors with one layout.
+    lse: [B, H, N] float32.  Buffers not given are allocated with torch.
+    """
+    import torch
+    scale = default_scale(q.shape[-1]) if scale is None else scale
+    _same_layout(q, k, v)
+    shape = _shape_of(q)
+    desc = make_desc(patterns, causal, scale)
+    ws_f, _ = ctypes.c_size_t(0), None
+    _check(lib().dla_plan_check(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(ws_f), None))
+    B, N, H, _ = q.shape
+    o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
+    _same_layout(q, o)
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if lse_t.shape != (B, H, N) or not lse_t.is_contiguous() or lse_t.dtype != torch.float32:
+        raise DlaError(DLA_E_INVALID, "lse must be a contiguous float32 [B, H, N] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(ws_f.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().dla_forward(ctypes.byref(desc), ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
+                             v.data_ptr(), o.data_ptr(), lse_t.data_ptr(), workspace.data_ptr(),
+                             workspace.numel(), _stream(stream, q.device)))
+    return o, lse_t
+
+
+def backward(q, k, v, o, lse, dout, patterns, causal=True, scale=None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * o) for dla forward outputs (o, lse)."""
+    import torch
+    scale = default_scale(q.shape[-1]) if scale is None else scale
+    _same_layout(q, k, v, o, dout)
+    shape = _shape_of(q)
+    desc = make_desc(patterns, causal, scale)
+    ws_b = ctypes.c_size_t(0)
+    _check(lib().dla_plan_check(ctypes.byref(desc), ctypes.byref(shape), None, ctypes.byref(ws_b)))
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        _same_layout(q, g)
+        grads.append(g)
+    if workspace is None:
+        workspace = torch.empty(max(ws_b.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().dla_backward(ctypes.byref(desc), ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
+                              v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                              grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), _stream(stream, q.device)))
+    return tuple(grads)
+
+
+def row_map(patterns, N, H, pattern, device="cuda", stream=None):
+    """Device int32 [H, N/r] map of sparse rows to original rows for one pattern."""
+    import torch
+    desc = make_desc(patterns, False, 1.0)
+    r = patterns[pattern][1]
+    out = torch.empty((H, N // r), dtype=torch.int32, device=device)
+    _check(lib().dla_row_map(ctypes.byref(desc), N, H, pattern, out.data_ptr(),
+                             _stream(stream, out.device)))
+    return out

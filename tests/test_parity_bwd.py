@@ -1,0 +1,97 @@
+"""GPU backward parity (dQ, dK, dV) against the CPU oracle's analytic backward.
+
+The GPU backward consumes the GPU forward's (o, lse), as the C ABI requires;
+the oracle runs its own forward and backward on the same seeded inputs.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_long_sequence_dilated_amd import dla, inputs
+from tests.gpu_util import ORACLE_WORKERS, TOL, normwise, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # (B, N, H, patterns, causal, layout)
+    (1, 512, 2, ((512, 1),), True, "bnhd"),                          # full causal attention
+    (2, 512, 3, ((128, 1), (256, 2), (512, 4)), True, "bnhd"),
+    (1, 900, 2, ((300, 1), (900, 3)), True, "bnhd"),                 # ragged 300-row segments
+    (1, 900, 2, ((300, 1), (900, 3)), False, "bnhd"),
+    (1, 512, 3, ((256, 2),), True, "bnhd"),                          # uncovered rows: zero grads
+    (1, 1024, 2, ((64, 1), (256, 4), (1024, 16)), True, "bnhd"),     # r > H
+    (1, 512, 2, ((128, 2), (128, 2), (512, 1)), True, "bnhd"),       # duplicate pattern
+    (1, 256, 3, ((4, 4), (64, 1)), True, "bnhd"),                    # one-row segments
+    (2, 512, 3, ((128, 1), (512, 4)), True, "bhnd"),                 # [B,H,N,D] storage
+    (1, 768, 2, ((768, 1), (768, 3)), False, "bnhd"),
+]
+
+
+def _run(q, k, v, do, pats, causal, scale, layout="bnhd", workers=1, ref_dtype=np.float64):
+    import torch
+    tq, tk, tv, tdo = (to_device(x, "bf16", layout) for x in (q, k, v, do))
+    o, lse = dla.forward(tq, tk, tv, pats, causal, scale)
+    dq, dk, dv = dla.backward(tq, tk, tv, o, lse, tdo, pats, causal, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, scale, dtype=ref_dtype, workers=workers)
+    refs = oracle.backward(q, k, v, o_ref, lse_ref, do, pats, causal, scale, dtype=ref_dtype,
+                           workers=workers)
+    errs = {}
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        errs[name] = normwise(to_host(got), ref)
+    return errs, (dq, dk, dv), refs
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}N{c[1]}H{c[2]}-{c[5]}-"
+                         f"{'c' if c[4] else 'nc'}-{'_'.join(f'{w}x{r}' for w, r in c[3])}")
+def test_backward_small_cases(case):
+    B, N, H, pats, causal, layout = case
+    print(f"case {case}", flush=True)
+    q, k, v, do = inputs.random_case(zlib.crc32(repr(case).encode()) & 0xFFFF, B, N, H, "bf16", 4)
+    errs, got, refs = _run(q, k, v, do, pats, causal, 0.125, layout)
+    print(errs, flush=True)
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
+    # rows that no pattern keeps have exactly zero gradient
+    n = np.arange(N)
+    for h in range(H):
+        kept = np.zeros(N, bool)
+        for w, r in pats:
+            kept |= (n % r) == (h % r)
+        for g in got:
+            assert np.all(to_host(g)[:, ~kept, h] == 0.0)
+
+
+def test_backward_c5_full_tensor():
+    import torch
+    wl = inputs.WORKLOADS["C5"]
+    print(wl.describe(), flush=True)
+    q, k, v, do = inputs.workload_inputs(wl)
+    errs, got, _ = _run(q, k, v, do, wl.patterns, True, wl.scale, workers=ORACLE_WORKERS,
+                        ref_dtype=np.float32)
+    print(f"C5: {errs}", flush=True)
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
+    # run-to-run determinism (no atomics anywhere)
+    tq, tk, tv, tdo = (to_device(x, "bf16") for x in (q, k, v, do))
+    o, lse = dla.forward(tq, tk, tv, wl.patterns, True)
+    again = dla.backward(tq, tk, tv, o, lse, tdo, wl.patterns, True)
+    torch.cuda.synchronize()
+    for a, b in zip(got, again):
+        assert torch.equal(a, b)
+
+
+def test_backward_rejects_fp32_and_small_workspace():
+    import torch
+    x = torch.zeros((1, 256, 2, 64), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((1, 2, 256), dtype=torch.float32, device="cuda")
+    with pytest.raises(dla.DlaError) as ei:
+        dla.backward(x, x, x, x, lse, x, [(64, 1)], True)
+    assert ei.value.code == dla.DLA_E_UNSUPPORTED
+    y = x.bfloat16()
+    with pytest.raises(dla.DlaError) as ei:
+        dla.backward(y, y, y, y, lse, y, [(64, 1)], True,
+                     workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
+    assert ei.value.code == dla.DLA_E_WORKSPACE
