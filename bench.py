@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of LongNet dilated attention on one MI355X (prints ONE JSON line).
+
+A step is one pass of the whole operator path over one batch already
+resident in HBM: dla_forward (attention over all patterns + merge) then
+dla_backward (preprocess + one launch per pattern), the operator's share of
+a training step.  Default workload: bf16, B=2, N=32768, H=12, D=64, causal,
+patterns w = 2048*2^i, r = 2^i for i = 0..4 (the 768-dim, 12-head model
+settings of the gptget.net LongNet summary, section 实验设计, at 32K tokens).
+
+Also reported, as extra fields of the same line:
+  * forward-only throughput at N=32768 (B=1) and N=1,048,576 (B=1);
+  * `roofline` of the kernel family that takes most of the timed region,
+    timed live with HIP events around its launches on the launch stream;
+  * `cpu_baseline`: the CPU oracle (float32, thread pool) on a bounded
+    sample of the same workload, scaled to the full workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s and % of bf16 MFMA peak, dilated attn fwd(+bwd), N=32K & 1M, 1 GPU"
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd_bf16.hip", "dla_device.h"],
+    "attn_bwd": ["attn_bwd_bf16.hip", "dla_device.h"],
+    "combine": ["combine.hip", "dla_device.h"],
+    "bwd_prep": ["bwd_misc.hip", "dla_device.h"],
+}
+
+
+def kernel_source_sha(family: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, "sparse_long_sequence_dilated_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def gpu_inputs(wl, count, seed):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return [torch.randn((wl.B, wl.N, wl.H, wl.D), device="cuda", generator=g).bfloat16()
+            for _ in range(count)]
+
+
+def family_work(family, wl, pairs):
+    """Algorithmic work of one step of a kernel family: (amount, unit, bound)."""
+    D = wl.D
+    if family == "attn_bwd":
+        return 10 * D * pairs, "flop", "mfma"
+    if family in ("attn_fwd", "attn_fwd_f32"):
+        return 4 * D * pairs, "flop", "mfma"
+    rows = wl.B * wl.N * wl.H
+    if family == "bwd_prep":
+        return rows * (2 * D * 2 + 4), "byte", "hbm"    # read O, dO (bf16), write D (fp32)
+    if family == "combine":
+        # rows kept by the primary pattern and >= 1 other: read O, LSE and each
+        # other pattern's partial (O_p bf16, LSE_p fp32); write O, LSE
+        period = math.lcm(*[r for _, r in wl.patterns])
+        total = 0
+        for h in range(wl.H):
+            for n_mod in range(period):
+                kept = [p for p, (w, r) in enumerate(wl.patterns) if n_mod % r == h % r]
+                if len(kept) < 2:
+                    continue
+                per = (2 * D * 2 + 8) + (len(kept) - 1) * (D * 2 + 4)
+                total += per * (wl.N // period)
+        return total * wl.B, "byte", "hbm"
+    raise KeyError(family)
+
+
+def traffic_for(family, launches_per_step):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(family)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_sha(family):
+        return None
+    return rec["bytes_per_step"] / max(1, launches_per_step) if rec.get("per") == "step" else rec.get("bytes_per_launch")
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    from sparse_long_sequence_dilated_amd import dla
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    dla.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dla.timing_enable(False)
+    fams = {}
+    for fam in ("attn_fwd", "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd"):
+        n, ms = dla.timing_collect(fam)
+        if n:
+            fams[fam] = (n, ms)
+    return (t1 - t0) * 1e3 / steps, fams
+
+
+def forward_only(name, steps, warmup):
+    import torch
+    from sparse_long_sequence_dilated_amd import dla, inputs
+    wl = inputs.WORKLOADS[name]
+    q, k, v = gpu_inputs(wl, 3, 1000 + wl.seed)
+    ws_f, _ = dla.plan_check(wl.patterns, wl.causal, wl.scale, wl.B, wl.N, wl.H)
+    ws = torch.empty(max(ws_f, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device="cuda")
+
+    def step():
+        dla.forward(q, k, v, wl.patterns, wl.causal, wl.scale, out=o, lse=lse, workspace=ws)
+
+    ms, fams = time_steps(step, steps, warmup)
+    pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
+    tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
+    out = {"workload": wl.describe(), "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "ms": ms,
+           "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS}
+    for fam, (n, fms) in fams.items():
+        out[f"{fam}_us_per_launch"] = 1e3 * fms / n
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(wl, heads=4):
+    """The oracle (float32, thread pool) on batch 0 and `heads` heads of the workload."""
+    import numpy as np
+
+    import oracle
+    from sparse_long_sequence_dilated_amd import inputs
+    workers = max(1, min(16, os.cpu_count() or 1))
+    q, k, v, do = inputs.draw((1, wl.N, heads, wl.D), wl.seed, 4, wl.dtype)
+    t0 = time.perf_counter()
+    o, lse = oracle.forward(q, k, v, wl.patterns, wl.causal, wl.scale, dtype=np.float32,
+                            workers=workers)
+    if wl.backward:
+        oracle.backward(q, k, v, o, lse, do, wl.patterns, wl.causal, wl.scale, dtype=np.float32,
+                        workers=workers)
+    t = time.perf_counter() - t0
+    scale = (wl.B * wl.H) / heads
+    return {"value": wl.B * wl.N / (t * scale), "unit": "tokens/s", "cores": workers,
+            "kind": "oracle",
+            "sample": (f"{'fwd+bwd' if wl.backward else 'fwd'} of batch 1 of {wl.B}, heads 0-{heads - 1} "
+                       f"of {wl.H}, full N={wl.N} and all patterns; float32 NumPy oracle, "
+                       f"{workers} threads, {t:.2f} s wall; scaled by {scale:g} to the full workload")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="C5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-forward-lines", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path, so --gpus must be 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_long_sequence_dilated_amd import dla, inputs
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+
+    wl = inputs.WORKLOADS[args.workload]
+    if wl.dtype != "bf16":
+        raise SystemExit("the step benchmark runs the bf16 workloads")
+    tensors = gpu_inputs(wl, 4, 1000 + wl.seed)
+    q, k, v, do = tensors
+    ws_f, ws_b = dla.plan_check(wl.patterns, wl.causal, wl.scale, wl.B, wl.N, wl.H)
+    ws_fwd = torch.empty(max(ws_f, 1), dtype=torch.uint8, device="cuda")
+    ws_bwd = torch.empty(max(ws_b, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def step():
+        dla.forward(q, k, v, wl.patterns, wl.causal, wl.scale, out=o, lse=lse, workspace=ws_fwd)
+        if wl.backward:
+            dla.backward(q, k, v, o, lse, do, wl.patterns, wl.causal, wl.scale, dq=dq, dk=dk,
+                         dv=dv, workspace=ws_bwd)
+
+    ms, fams = time_steps(step, args.steps, args.warmup)
+    pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
+    flops = (14 if wl.backward else 4) * wl.D * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    dom = max(fams, key=lambda f: fams[f][1])
+    n_launch, dom_ms = fams[dom]
+    work, unit, bound = family_work(dom, wl, pairs)
+    launches_per_step = n_launch / args.steps
+    avg_launch_s = dom_ms * 1e-3 / n_launch
+    per_launch = work / launches_per_step
+    if unit == "flop":
+        achieved, peak, runit = per_launch / avg_launch_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, runit = per_launch / avg_launch_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    roofline = {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": runit,
+                "frac": achieved / peak, "traffic": traffic_for(dom, launches_per_step),
+                "launches_per_step": launches_per_step, "avg_launch_us": avg_launch_s * 1e6,
+                "work_per_step": work, "work_unit": unit}
+    kernels = {f: {"launches_per_step": n / args.steps, "us_per_step": 1e3 * t / args.steps}
+               for f, (n, t) in fams.items()}
+    del tensors, q, k, v, do, ws_fwd, ws_bwd, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+    extra = []
+    if not args.no_forward_lines:
+        extra.append(forward_only("C3", max(5, args.steps), args.warmup))
+        extra.append(forward_only("C4", max(3, args.steps // 4), 1))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+
+    line = {
+        "metric": METRIC, "value": wl.B * wl.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.describe(), "B": wl.B, "N": wl.N, "H": wl.H, "D": wl.D,
+                   "patterns": [list(p) for p in wl.patterns], "causal": wl.causal,
+                   "step": "dla_forward + dla_backward" if wl.backward else "dla_forward"},
+        "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        "roofline": roofline, "kernels": kernels, "forward_only": extra, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,7 +31,8 @@
  *     pointers are not checked and may be null.
  *   - The caller owns every buffer, including the workspace; the library
  *     allocates and frees nothing, keeps no device state and never
- *     synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     synchronises (apart from dla_timing_collect, which waits for its
+ *     events).  Work is enqueued on `stream` (a hipStream_t; NULL is the
  *     null stream) and returns before it runs.
  *   - Descriptors are caller-owned host memory read only during the call.
  *   - Return value: DLA_OK or a negative DLA_E_* code.  All validation runs on
@@ -133,6 +134,22 @@ int dla_row_map(const dla_desc* desc, int64_t N, int32_t H, int32_t pattern, int
  * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
  */
 int dla_pair_count(const dla_desc* desc, const dla_shape* shape, int64_t* pairs);
+
+/*
+ * Opt-in launch timing, a profiling aid.  While enabled (on != 0), every
+ * kernel launch made by dla_forward / dla_backward is bracketed by two HIP
+ * events recorded on the caller's stream (host-side bookkeeping only; the
+ * kernels are unchanged).  Kernel families: "attn_fwd" (bf16 forward
+ * attention), "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd".
+ */
+int dla_timing_enable(int on);
+
+/*
+ * Wait for the recorded events of kernel family `name`, return the number of
+ * timed launches and their summed duration in milliseconds, and forget them.
+ * Errors: DLA_E_INVALID (null argument), DLA_E_HIP.
+ */
+int dla_timing_collect(const char* name, int64_t* launches, double* total_ms);
 
 /* Static text for an error code. */
 const char* dla_strerror(int code);

@@ -389,6 +389,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_bf16_kernel(const AttnBwdArgs
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const int64_t total = a.sched_kv.total + a.sched_q.total;
   if (total == 0) return hipSuccess;
+  TimedLaunch tl("attn_bwd", stream);
   hipLaunchKernelGGL(attn_bwd_bf16_kernel, dim3((unsigned)total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

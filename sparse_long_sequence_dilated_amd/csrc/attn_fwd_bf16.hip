@@ -232,6 +232,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream) {
   if (a.sched.total == 0) return hipSuccess;
+  TimedLaunch tl("attn_fwd", stream);
   hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)a.sched.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const AttnFwdArgs a) 
 
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a, hipStream_t stream) {
   if (a.sched.total == 0) return hipSuccess;
+  TimedLaunch tl("attn_fwd_f32", stream);
   hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3((unsigned)a.sched.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -110,6 +110,7 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream) {
   const int64_t threads = a.B * a.N * a.H * 8;
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256));
+  TimedLaunch tl("combine", stream);
   if (dtype == DLA_F32)
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, stream, a);
   else

@@ -86,6 +86,22 @@ struct BwdPrepArgs {
   int zero_uncovered;      // write zero gradients for rows no pattern keeps
 };
 
+// Scope guard of the opt-in launch timing (dla_timing_enable): records HIP
+// events on `stream` around the launches made inside its lifetime.
+class TimedLaunch {
+ public:
+  TimedLaunch(const char* name, hipStream_t stream);
+  ~TimedLaunch();
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+  bool active_ = false;
+};
+
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);

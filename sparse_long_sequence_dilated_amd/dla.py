@@ -25,7 +25,7 @@ MAX_PATTERNS = 16
 HEAD_DIM = 64
 
 EXPORTS = ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
-           "dla_strerror", "dla_last_error")
+           "dla_timing_enable", "dla_timing_collect", "dla_strerror", "dla_last_error")
 
 
 class DlaError(RuntimeError):
@@ -68,6 +68,11 @@ def lib():
     L.dla_backward.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dla_row_map.argtypes = [pd, i64, i32, i32, vp, vp]
     L.dla_pair_count.argtypes = [pd, ps, ctypes.POINTER(i64)]
+    L.dla_timing_enable.argtypes = [ctypes.c_int]
+    L.dla_timing_enable.restype = ctypes.c_int
+    L.dla_timing_collect.argtypes = [ctypes.c_char_p, ctypes.POINTER(i64),
+                                     ctypes.POINTER(ctypes.c_double)]
+    L.dla_timing_collect.restype = ctypes.c_int
     L.dla_strerror.argtypes = [ctypes.c_int]
     L.dla_strerror.restype = ctypes.c_char_p
     L.dla_last_error.argtypes = []
@@ -209,6 +214,18 @@ def backward(q, k, v, o, lse, dout, patterns, causal=True, scale=None, dq=None, 
                               grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
                               workspace.data_ptr(), workspace.numel(), _stream(stream, q.device)))
     return tuple(grads)
+
+
+def timing_enable(on: bool = True):
+    """Bracket every library kernel launch with HIP events (profiling aid)."""
+    _check(lib().dla_timing_enable(int(bool(on))))
+
+
+def timing_collect(name: str):
+    """(launches, total_ms) of the timed launches of kernel family `name`; forgets them."""
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(lib().dla_timing_collect(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 def row_map(patterns, N, H, pattern, device="cuda", stream=None):
