@@ -21,6 +21,7 @@ namespace dla {
 
 constexpr int kFwdBM = 256;  // sparse query rows per workgroup
 constexpr int kFwdBN = 64;   // keys per tile
+constexpr float kLazyLog2 = 8.f;  // rescale only when a row max grows by > 2^8
 
 struct __align__(16) FwdSmem {
   uint4 k[2][kFwdBN * 8];   // R layout
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
             s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[qb][ks], s[kb][qb], 0, 0, 0);
         }
       }
+      bf16x8 pop[2][4];
       const int k0 = kt * kFwdBN;
       const bool need_mask = (k0 + kFwdBN > L) || (a.causal && k0 + kFwdBN > qw0);
       if (need_mask) {
@@ -144,50 +146,53 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
       }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        // Row max of this tile (both lane halves hold the same query row).
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-        mx = xhalf_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx * c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-        m_run[qb] = m_new;
-        float rs = 0.f;
+        mx = xhalf_max(mx) * c;
+        // Lazy rescaling: keep the running maximum unless this tile exceeds it
+        // by more than 2^kLazyLog2 (P then stays <= 2^kLazyLog2, harmless for
+        // bf16 and fp32).  The result is the same softmax; only the shared
+        // exponent offset differs.  Rare after the first tile.
+        if (__builtin_amdgcn_ballot_w64(mx > m_run[qb] + kLazyLog2) != 0) {
+          const float m_new = fmaxf(m_run[qb], mx);
+          const float alpha = (m_run[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][e], c, -m_use));
-            s[kb][qb][e] = pv;
-            rs += pv;
-          }
-        l_run[qb] = l_run[qb] * alpha + rs;
+            for (int e = 0; e < 16; ++e) oacc[db][qb][e] *= alpha;
+        }
+        const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+        // P in bf16 as the MFMA B operand; the row sum adds the same rounded
+        // values (v_dot2c_f32_bf16 with (1, 1)), in four independent chains.
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][qb][e] *= alpha;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 pop[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int kk = 0; kk < 4; ++kk) {
           const f32x16& sv = s[kk >> 1][qb];
           const int e0 = 8 * (kk & 1);
           uint32_t wds[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wds[i] = pack_bf16(sv[e0 + 2 * i], sv[e0 + 2 * i + 1]);
-          pop[qb] = __builtin_bit_cast(bf16x8, uint4{wds[0], wds[1], wds[2], wds[3]});
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e0 + 2 * i], c, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e0 + 2 * i + 1], c, -m_use));
+            wds[i] = pack_bf16(p0, p1);
+            rs[i] = dot2_bf16_ones(wds[i], rs[i]);
+          }
+          pop[qb][kk] = __builtin_bit_cast(bf16x8, uint4{wds[0], wds[1], wds[2], wds[3]});
         }
+        l_run[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const bf16x8 vop = *(const bf16x8*)&sm.vt[buf][t_chunk(32 * db + li, kk, lg)];
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[qb], oacc[db][qb], 0, 0, 0);
-        }
+          for (int db = 0; db < 2; ++db) {
+            const bf16x8 vop = *(const bf16x8*)&sm.vt[buf][t_chunk(32 * db + li, kk, lg)];
+            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[qb][kk], oacc[db][qb], 0, 0, 0);
+          }
       }
     }
     if (kt + 1 < nkt) store_tile(buf ^ 1);

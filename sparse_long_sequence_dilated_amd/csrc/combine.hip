@@ -10,8 +10,10 @@
 //
 // The pattern that keeps the most rows wrote straight into o/lse; this pass
 // touches only rows that another pattern also keeps (or that none keeps) and
-// merges in place.  Eight lanes per (b, n, h) row, eight d values each; rows
-// are walked in [B, N, H] order so that o is read and written contiguously.
+// merges in place.  A workgroup takes 32 consecutive rows of one (batch,
+// head), eight lanes per row and eight d values per lane, so the LSE and
+// partial-LSE reads are contiguous; all index arithmetic is 32-bit, with
+// shifts for power-of-two rates.
 #include "dla_device.h"
 
 namespace dla {
@@ -46,59 +48,78 @@ struct Vec8<__bf16> {
   }
 };
 
+// n / r and n mod r for the small set of rates of a launch (shift >= 0 for powers of two).
+__device__ __forceinline__ void divmod_r(uint32_t n, uint32_t r, int shift, uint32_t& q, uint32_t& m) {
+  if (shift >= 0) {
+    q = n >> shift;
+    m = n & (r - 1);
+  } else {
+    q = n / r;
+    m = n - q * r;
+  }
+}
+
+// Block = 32 consecutive rows n of one (batch, head); 8 lanes per row.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid >> 3;
-  const int c = gid & 7;
-  if (row >= a.B * a.N * a.H) return;
-  const int h = (int)(row % a.H);
-  const int64_t bn = row / a.H;
-  const int64_t n = bn % a.N;
-  const int64_t b = bn / a.N;
+  const uint32_t b = blockIdx.x / a.nblk;
+  const uint32_t n = (blockIdx.x - b * a.nblk) * 32 + (threadIdx.x >> 3);
+  const int c = threadIdx.x & 7;
+  const uint32_t h = blockIdx.y;
+  if (n >= (uint32_t)a.N) return;
 
-  const int rp = a.r[a.prim];
-  const bool prim_kept = (n % rp) == (h % rp);
-  int others = 0;
-  for (int p = 0; p < a.P; ++p)
-    if (p != a.prim && (n % a.r[p]) == (h % a.r[p])) ++others;
-  if (prim_kept && others == 0) return;
-
-  const int64_t bh = b * a.H + h;
-  T* orow = (T*)a.o + b * a.sb + n * a.sn + h * a.sh + 8 * c;
-  float* lse_dst = a.lse + bh * a.N + n;
-  const float l_prim = prim_kept ? *lse_dst : -INFINITY;
-  float mx = l_prim;
-  for (int p = 0; p < a.P; ++p) {
-    if (p == a.prim || (n % a.r[p]) != (h % a.r[p])) continue;
-    mx = fmaxf(mx, a.part_lse[p][bh * (a.N / a.r[p]) + n / a.r[p]]);
+  uint32_t kept = 0, sidx[kMaxP];
+#pragma unroll
+  for (int p = 0; p < kMaxP; ++p) {
+    sidx[p] = 0;
+    if (p < a.P) {
+      uint32_t q, m, qh, mh;
+      divmod_r(n, (uint32_t)a.r[p], a.shift[p], q, m);
+      divmod_r(h, (uint32_t)a.r[p], a.shift[p], qh, mh);
+      if (m == mh) {
+        kept |= 1u << p;
+        sidx[p] = q;  // sparse index of row n in pattern p
+      }
+    }
   }
+  const uint32_t prim_bit = 1u << a.prim;
+  if (kept == prim_bit) return;  // only the pattern that wrote o keeps this row
+
+  const int64_t bh = (int64_t)b * a.H + h;
+  T* orow = (T*)a.o + (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
+  float* lse_dst = a.lse + bh * a.N + n;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  if (mx == -INFINITY) {  // no pattern keeps this row
+  if (kept == 0) {  // no pattern keeps this row
     Vec8<T>::store(orow, acc);
     if (c == 0) *lse_dst = -INFINITY;
     return;
   }
-  float tot = prim_kept ? expf(l_prim - mx) : 0.f;
-  for (int p = 0; p < a.P; ++p) {
-    if (p == a.prim || (n % a.r[p]) != (h % a.r[p])) continue;
-    tot += expf(a.part_lse[p][bh * (a.N / a.r[p]) + n / a.r[p]] - mx);
+  float lv[kMaxP];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kMaxP; ++p) {
+    lv[p] = -INFINITY;
+    if (kept & (1u << p)) {
+      lv[p] = (p == a.prim) ? *lse_dst : a.part_lse[p][bh * (a.N / a.r[p]) + sidx[p]];
+      mx = fmaxf(mx, lv[p]);
+    }
   }
+  float tot = 0.f;
+#pragma unroll
+  for (int p = 0; p < kMaxP; ++p)
+    if (kept & (1u << p)) tot += expf(lv[p] - mx);
   const float lse = mx + logf(tot);
   float v[8];
-  if (prim_kept) {
-    const float wt = expf(l_prim - lse);
-    Vec8<T>::load(orow, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = wt * v[i];
-  }
-  for (int p = 0; p < a.P; ++p) {
-    if (p == a.prim || (n % a.r[p]) != (h % a.r[p])) continue;
-    const int64_t m = bh * (a.N / a.r[p]) + n / a.r[p];
-    const float wt = expf(a.part_lse[p][m] - lse);
-    Vec8<T>::load((const T*)a.part_o[p] + m * kD + 8 * c, v);
+  for (int p = 0; p < kMaxP; ++p) {
+    if (!(kept & (1u << p))) continue;
+    const float wt = expf(lv[p] - lse);
+    if (p == a.prim)
+      Vec8<T>::load(orow, v);
+    else
+      Vec8<T>::load((const T*)a.part_o[p] + (bh * (a.N / a.r[p]) + sidx[p]) * kD + 8 * c, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wt, v[i], acc[i]);
   }
@@ -107,9 +128,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream) {
-  const int64_t threads = a.B * a.N * a.H * 8;
-  if (threads == 0) return hipSuccess;
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (a.B * a.N * a.H == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.B * a.nblk), (unsigned)a.H);
   TimedLaunch tl("combine", stream);
   if (dtype == DLA_F32)
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, stream, a);

@@ -91,6 +91,14 @@ extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const v
     cb.H = pl.H;
     cb.P = pl.P;
     cb.prim = pl.prim;
+    for (int i = 0; i < pl.P; ++i) {
+      const int r = pl.r[i];
+      cb.shift[i] = (r & (r - 1)) ? -1 : __builtin_ctz((unsigned)r);
+    }
+    const int64_t nblk = (pl.N + 31) / 32;
+    if (nblk * pl.B > 0x7FFFFFFF)
+      return fail(DLA_E_UNSUPPORTED, "B * N / 32 exceeds the launch grid");
+    cb.nblk = (uint32_t)nblk;
     e = launch_combine(cb, pl.dtype, st);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }

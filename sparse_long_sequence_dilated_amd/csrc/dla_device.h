@@ -71,6 +71,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float dot2_bf16_ones(uint32_t packed, float acc) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2v;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, packed),
+                                         __builtin_bit_cast(bf16x2v, 0x3F803F80u), acc, false);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return as_float(x & 0xFFFF0000u); }
 

@@ -36,6 +36,8 @@ struct CombineArgs {
   int64_t B, N, H;
   int P, prim;
   int r[kMaxP];
+  int shift[kMaxP];        // log2(r) when r is a power of two, else -1
+  uint32_t nblk;           // row blocks of 32 per (batch, head)
 };
 
 struct RowMapArgs {
