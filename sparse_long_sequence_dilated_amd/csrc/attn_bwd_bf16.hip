@@ -113,7 +113,7 @@ __device__ void bwd_kv_unit(const AttnBwdArgs& a, BwdKVSmem* sm, int64_t unit) {
   const int li = lane & 31, lg = lane >> 5;
   int pp, b, h, tile;
   int64_t seg;
-  decode_unit(a.sched_kv, unit, a.B, a.H, &a.nseg, pp, b, h, seg, tile);
+  decode_unit(a.sched_kv, (uint32_t)unit, (int)a.H, &a.nseg, pp, b, h, seg, tile);
   const int w = a.w, r = a.r, L = a.L;
   // Under a causal mask a key tile's work shrinks with its index: run low tiles first.
   if (a.causal) tile = (L + kBwdT - 1) / kBwdT - 1 - tile;
@@ -260,7 +260,7 @@ __device__ void bwd_q_unit(const AttnBwdArgs& a, BwdQSmem* sm, int64_t unit) {
   const int li = lane & 31, lg = lane >> 5;
   int pp, b, h, tile;
   int64_t seg;
-  decode_unit(a.sched_q, unit, a.B, a.H, &a.nseg, pp, b, h, seg, tile);
+  decode_unit(a.sched_q, (uint32_t)unit, (int)a.H, &a.nseg, pp, b, h, seg, tile);
   const int w = a.w, r = a.r, L = a.L;
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;

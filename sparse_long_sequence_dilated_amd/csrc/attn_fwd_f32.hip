@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const AttnFwdArgs a) 
   const int tid = threadIdx.x;
   int p, b, h, tile;
   int64_t seg;
-  decode_unit(a.sched, blockIdx.x, a.B, a.H, a.nseg, p, b, h, seg, tile);
+  decode_unit(a.sched, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile);
   const int w = a.w[p], r = a.r[p], L = a.L[p];
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const AttnFwdArgs a) 
     dst = (float*)a.o + head_off + n * a.sn;
     lse_dst = a.lse + bh * a.N + n;
   } else {
-    const int64_t nsparse = a.N / r;
+    const int64_t nsparse = a.nsp[p];
     const int64_t m = seg * L + row;
     dst = (float*)a.part_o[p] + (bh * nsparse + m) * kD;
     lse_dst = a.part_lse[p] + bh * nsparse + m;

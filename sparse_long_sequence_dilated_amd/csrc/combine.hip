@@ -22,9 +22,15 @@ template <typename T>
 struct Vec8;
 template <>
 struct Vec8<float> {
-  static __device__ __forceinline__ void load(const float* p, float v[8]) {
-    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  struct Raw {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ Raw load_raw(const float* p) {
+    return Raw{*(const float4*)p, *(const float4*)(p + 4)};
+  }
+  static __device__ __forceinline__ void unpack(const Raw& r, float v[8]) {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
   }
   static __device__ __forceinline__ void store(float* p, const float v[8]) {
     *(float4*)p = float4{v[0], v[1], v[2], v[3]};
@@ -33,8 +39,9 @@ struct Vec8<float> {
 };
 template <>
 struct Vec8<__bf16> {
-  static __device__ __forceinline__ void load(const __bf16* p, float v[8]) {
-    const uint4 a = *(const uint4*)p;
+  typedef uint4 Raw;
+  static __device__ __forceinline__ Raw load_raw(const __bf16* p) { return *(const uint4*)p; }
+  static __device__ __forceinline__ void unpack(const Raw& a, float v[8]) {
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -96,30 +103,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     if (c == 0) *lse_dst = -INFINITY;
     return;
   }
+  // Issue every load first (LSE and the 8-value slice of each kept pattern's
+  // output), so the memory latencies overlap; then merge.
   float lv[kMaxP];
-  float mx = -INFINITY;
+  typename Vec8<T>::Raw raw[kMaxP];
 #pragma unroll
   for (int p = 0; p < kMaxP; ++p) {
     lv[p] = -INFINITY;
     if (kept & (1u << p)) {
-      lv[p] = (p == a.prim) ? *lse_dst : a.part_lse[p][bh * (a.N / a.r[p]) + sidx[p]];
-      mx = fmaxf(mx, lv[p]);
+      if (p == a.prim) {
+        lv[p] = *lse_dst;
+        raw[p] = Vec8<T>::load_raw(orow);
+      } else {
+        const int64_t m = bh * a.nsp[p] + sidx[p];
+        lv[p] = a.part_lse[p][m];
+        raw[p] = Vec8<T>::load_raw((const T*)a.part_o[p] + m * kD + 8 * c);
+      }
     }
   }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kMaxP; ++p) mx = fmaxf(mx, lv[p]);
   float tot = 0.f;
 #pragma unroll
   for (int p = 0; p < kMaxP; ++p)
     if (kept & (1u << p)) tot += expf(lv[p] - mx);
   const float lse = mx + logf(tot);
-  float v[8];
 #pragma unroll
   for (int p = 0; p < kMaxP; ++p) {
     if (!(kept & (1u << p))) continue;
     const float wt = expf(lv[p] - lse);
-    if (p == a.prim)
-      Vec8<T>::load(orow, v);
-    else
-      Vec8<T>::load((const T*)a.part_o[p] + (bh * (a.N / a.r[p]) + sidx[p]) * kD + 8 * c, v);
+    float v[8];
+    Vec8<T>::unpack(raw[p], v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wt, v[i], acc[i]);
   }

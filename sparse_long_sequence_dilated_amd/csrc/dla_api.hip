@@ -36,6 +36,7 @@ static void fill_fwd_args(const Plan& pl, AttnFwdArgs* a) {
     a->r[i] = pl.r[i];
     a->L[i] = pl.L[i];
     a->nseg[i] = pl.nseg[i];
+    a->nsp[i] = pl.N / pl.r[i];
   }
 }
 
@@ -71,6 +72,7 @@ extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const v
     a.part_lse[i] = (float*)((char*)ws + pl.part_lse_off[i]);
   }
   make_schedule(pl, pl.dtype == DLA_BF16 ? 256 : 64, &a.sched);
+  if (a.sched.total > 0x7FFFFFFF) return fail(DLA_E_UNSUPPORTED, "too many work units for one launch");
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = pl.dtype == DLA_BF16 ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_f32(a, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -82,6 +84,7 @@ extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const v
       cb.part_o[i] = a.part_o[i];
       cb.part_lse[i] = a.part_lse[i];
       cb.r[i] = pl.r[i];
+      cb.nsp[i] = pl.N / pl.r[i];
     }
     cb.sb = pl.sb;
     cb.sn = pl.sn;

@@ -106,6 +106,8 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
     one.nseg[0] = pl.nseg[p];
     make_schedule(one, 128, &a.sched_kv);
     make_schedule(one, 128, &a.sched_q);
+    if (a.sched_kv.total + a.sched_q.total > 0x7FFFFFFF)
+      return fail(DLA_E_UNSUPPORTED, "too many work units for one launch");
     e = launch_attn_bwd_bf16(a, st);
     if (e != hipSuccess) return fail(DLA_E_HIP, "backward launch: %s", hipGetErrorString(e));
   }

@@ -25,27 +25,29 @@ __device__ __forceinline__ int64_t seg_base_row(int64_t seg, int w, int r, int h
   return seg * (int64_t)w + (h % r);
 }
 
-// Longest-first unit decode (see Schedule in dla_plan.h).
-__device__ __forceinline__ void decode_unit(const Schedule& s, int64_t u, int64_t B, int64_t H,
+// Longest-first unit decode (see Schedule in dla_plan.h).  All quantities fit
+// in 32 bits (the planner bounds the unit count by the launch grid), so the
+// divisions are 32-bit.
+__device__ __forceinline__ void decode_unit(const Schedule& s, uint32_t u, int H,
                                             const int64_t* nseg, int& p, int& b, int& h,
                                             int64_t& seg, int& tile) {
   int j = 0;
-  while (j + 1 < s.nband && u >= s.band_start[j + 1]) ++j;
-  const int64_t rel = u - s.band_start[j];
-  const int64_t per_level = s.cum[s.band_npat[j]];
-  const int64_t lvl = rel / per_level;
-  int64_t rem = rel - lvl * per_level;
+  while (j + 1 < s.nband && u >= (uint32_t)s.band_start[j + 1]) ++j;
+  const uint32_t rel = u - (uint32_t)s.band_start[j];
+  const uint32_t per_level = (uint32_t)s.cum[s.band_npat[j]];
+  const uint32_t lvl = rel / per_level;
+  uint32_t rem = rel - lvl * per_level;
   tile = s.band_hi[j] - 1 - (int)lvl;
   int i = 0;
-  while (rem >= s.cum[i + 1]) ++i;
+  while (rem >= (uint32_t)s.cum[i + 1]) ++i;
   p = s.order[i];
-  rem -= s.cum[i];
-  const int64_t ns = nseg[p];
-  seg = rem % ns;
+  rem -= (uint32_t)s.cum[i];
+  const uint32_t ns = (uint32_t)nseg[p];
+  const uint32_t sg = rem % ns;
   rem /= ns;
-  h = (int)(rem % H);
-  b = (int)(rem / H);
-  (void)B;
+  h = (int)(rem % (uint32_t)H);
+  b = (int)(rem / (uint32_t)H);
+  seg = sg;
 }
 
 // Bit-cast helpers.
@@ -84,9 +86,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return as_float(x & 0xFFF
 // LDS layouts of a 64-row x 64-column bf16 tile (rows = sequence, cols = d).
 //
 // Row-major ("R"): 64 rows of 8 16-byte chunks; chunk c of row i is stored at
-// chunk position c ^ (i & 7) so that the 32 lanes of an MFMA operand read
-// (one row each, same logical chunk) spread over all banks.
-__device__ __forceinline__ int r_index(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// chunk position c ^ t_swz(i).  The 32 lanes of an MFMA operand read (one row
+// each, same logical chunk) then hit distinct 16-byte bank groups both within
+// any 8 consecutive rows (32 banks x 4 bytes) and within any 16 consecutive
+// rows taken modulo 256 bytes (64 banks x 4 bytes).
+__device__ __forceinline__ int t_swz(int d);
+__device__ __forceinline__ int r_index(int row, int chunk) { return row * 8 + (chunk ^ t_swz(row)); }
 
 // Transposed ("T"): 64 d-rows of 32 words; each word packs the values of two
 // consecutive sequence rows.  Within each block of 16 sequence rows the order

@@ -23,6 +23,7 @@ struct AttnFwdArgs {
   float scale_log2;        // scale * log2(e)
   int w[kMaxP], r[kMaxP], L[kMaxP];
   int64_t nseg[kMaxP];
+  int64_t nsp[kMaxP];      // N / r: sparse rows per (batch, head) of each pattern
   Schedule sched;
 };
 
@@ -36,6 +37,7 @@ struct CombineArgs {
   int64_t B, N, H;
   int P, prim;
   int r[kMaxP];
+  int64_t nsp[kMaxP];      // N / r
   int shift[kMaxP];        // log2(r) when r is a power of two, else -1
   uint32_t nblk;           // row blocks of 32 per (batch, head)
 };
