@@ -40,12 +40,6 @@ constexpr int kFwdBN = 64;       // keys per LDS tile (two 32-key half tiles)
 constexpr int kStages = 4;       // LDS ring depth (tiles in flight: 3)
 constexpr float kSumLimit = 65536.f;
 
-typedef __attribute__((address_space(3))) uint4 lds_u4;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(1))) void glb_void;
-
 struct __align__(16) FwdStage {
   uint4 k[kFwdBN * 8];  // 8 KB
   uint4 v[kFwdBN * 8];  // 8 KB

@@ -114,6 +114,55 @@ __device__ __forceinline__ int t_chunk(int d, int kk, int g) {
   return d * 8 + ((2 * kk + g) ^ t_swz(d));
 }
 
+// Swizzle of the 16-byte chunks of a 64-row x 128-byte LDS tile that is read
+// both row-wise (32 lanes on 32 consecutive rows, one chunk each, as an MFMA
+// operand) and transposed (ds_read_b64_tr_b16 over 4-row groups): chunk c of
+// row i lives at c ^ u_swz(i).  Both access kinds are bank-conflict-free with
+// 32 banks x 4 bytes and with 64 banks x 4 bytes.
+__device__ __forceinline__ int u_swz(int row) {
+  return (((row & 3) << 1) | ((row >> 2) & 1)) ^ (((row >> 3) & 1) << 1);
+}
+
+typedef __attribute__((address_space(3))) uint4 lds_u4;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(1))) void glb_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte operand read of a u-swizzled tile (byte offset within the tile).
+__device__ __forceinline__ bf16x8 lds_read_b128(const lds_u4* base, int byte_off) {
+  return __builtin_bit_cast(bf16x8, *(const lds_u4*)((const lds_char*)base + byte_off));
+}
+// MFMA operand with 8 consecutive sequence rows of one head dimension from a
+// row-major u-swizzled tile: two transposed 8-byte reads (rows +0..3 and +8..11
+// relative to the lane's address), matching the k-slot order of an operand
+// that comes from a 32x32 accumulator.
+__device__ __forceinline__ bf16x8 lds_read_tr8(const lds_u4* base, int byte_off) {
+  const lds_char* p = (const lds_char*)base + byte_off;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * 128));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Per-lane byte offset of lds_read_tr8 for head-dimension block db (32 dims)
+// and 16-row k-step kk of a 64-row tile: lane l = 16m + t supplies row
+// 16kk + 8*half + 4*(m/2) + t/4 and dims 32db + 16(m%2) + 4(t%4) .. +4, and
+// receives rows (16kk + 4*(l/32)) + {0..3, 8..11} of head dim 32db + l%32.
+// The k-step enters as + kk*16*128 (u_swz depends on row % 16 only).
+__device__ __forceinline__ int tr_offset(int lane, int db) {
+  const int t = lane & 15, m = lane >> 4;
+  const int row = 4 * (m >> 1) + (t >> 2);
+  const int chunk = 4 * db + 2 * (m & 1) + ((t & 3) >> 1);
+  return row * 128 + ((chunk ^ u_swz(row)) << 4) + 8 * (t & 1);
+}
+// Per-lane byte offset of the row-wise operand read: row 32*blk + (lane%32),
+// logical chunk 2*ks + lane/32.
+__device__ __forceinline__ int row_offset(int lane, int blk, int ks) {
+  const int row = 32 * blk + (lane & 31);
+  return row * 128 + (((2 * ks + (lane >> 5)) ^ u_swz(row)) << 4);
+}
+
 // Pack two rows' 16-byte chunks (8 bf16 each, same d range) into the 8 words
 // (row0[j], row1[j]) for j = 0..7.
 __device__ __forceinline__ void pack_pairs(const uint4& r0, const uint4& r1, uint32_t out[8]) {
