@@ -10,13 +10,22 @@
 // with rows gathered by the same strided address generator as the forward.
 //
 // One launch per pattern holds two kinds of workgroups (4 waves each):
-//   * key-tile units (128 keys, 32 per wave) loop over query tiles of 64 rows
-//     and accumulate dK^T = Q^T dS and dV^T = dO^T P in registers;
-//   * query-tile units (128 queries, 32 per wave) loop over key tiles of 64
-//     rows and accumulate dQ^T = K^T dS^T.
-// S (or S^T) comes out of v_mfma_f32_32x32x16_bf16 with the lane on the key
-// (or query) axis, so P and dS feed the next MFMA as B operands without any
-// data movement; the other operand is an LDS tile transposed when staged.
+//   * key units own 128 keys (32 per wave), stream the segment's query rows
+//     (Q, dO, and the (LSE, D) pairs) and accumulate dK^T = Q^T dS and
+//     dV^T = dO^T P in registers;
+//   * query units own 128 queries (32 per wave), stream key rows (K, V) and
+//     accumulate dQ^T = K^T dS^T.
+// The owned rows sit in registers as MFMA B operands; the streamed rows go
+// from HBM into a 4-stage LDS ring with buffer_load ... lds (one 64-row tile
+// per stage, three tiles ahead), in one u-swizzled row-major copy that serves
+// both the row-wise operand reads (ds_read_b128) and the transposed ones
+// (ds_read_b64_tr_b16) without bank conflicts.  S and dP come out of
+// v_mfma_f32_32x32x16_bf16 with the lane on the owned row, so P and dS feed
+// the next MFMA as B operands straight from registers.
+//
+// Work runs on 32-row halves h of the streamed side in a three-stage software
+// pipeline: phase h issues the MFMAs of half h+1 (S, dP) and of half h-1 (the
+// gradient products) while the VALU computes P and dS of half h.
 //
 // Patterns run one launch after another.  Per output row the epilogue looks
 // up which other patterns keep that row: the first pattern to touch it writes
@@ -26,25 +35,14 @@
 
 namespace dla {
 
-constexpr int kBwdT = 128;  // rows per unit (4 waves x 32)
-constexpr int kBwdS = 64;   // rows per streamed tile
+constexpr int kBwdRows = 128;   // rows a unit owns (4 waves x 32)
+constexpr int kBwdTile = 64;    // streamed rows per LDS tile
+constexpr int kBwdStages = 4;   // LDS ring depth (tiles in flight: 2)
 
-struct __align__(16) BwdKVSmem {   // staged query tile (for key-tile units)
-  uint4 q[kBwdS * 8];              // R layout
-  uint4 qt[kD * 8];                // T layout
-  uint4 d[kBwdS * 8];              // dO, R layout
-  uint4 dt[kD * 8];                // dO, T layout
-  float lse2[kBwdS];               // LSE * log2(e)
-  float delta[kBwdS];
-};
-struct __align__(16) BwdQSmem {    // staged key tile (for query-tile units)
-  uint4 k[kBwdS * 8];              // R layout
-  uint4 kt[kD * 8];                // T layout
-  uint4 v[kBwdS * 8];              // R layout
-};
-union __align__(16) BwdSmem {
-  BwdKVSmem kv[2];
-  BwdQSmem qs[2];
+struct __align__(16) BwdStage {
+  uint4 a[kBwdTile * 8];   // Q (key units) or K (query units): 64 rows x 128 B
+  uint4 b[kBwdTile * 8];   // dO (key units) or V (query units)
+  float2 ld[kBwdTile];     // key units: (LSE * log2 e, D) of the tile's rows
 };
 
 // bit 0: a pattern processed earlier keeps row n of head h; bit 1: a later one does.
@@ -76,47 +74,24 @@ __device__ __forceinline__ void emit4(int st, float* acc_row, __bf16* out_row, i
   }
 }
 
-// Stage rows [r0, r0+64) of a gathered tensor: thread loads rows 2*(tid/8)
-// and +1, chunk tid%8; writes R layout and (optionally) T layout.
-__device__ __forceinline__ void load_pair(const __bf16* base, int64_t rstride, int r0, int L,
-                                          int tid, uint4& a0, uint4& a1) {
-  const int c = tid & 7, rr = 2 * (tid >> 3);
-  const int ra = r0 + rr, rb = ra + 1;
-  a0 = ra < L ? *(const uint4*)(base + (int64_t)ra * rstride + 8 * c) : uint4{0, 0, 0, 0};
-  a1 = rb < L ? *(const uint4*)(base + (int64_t)rb * rstride + 8 * c) : uint4{0, 0, 0, 0};
-}
-__device__ __forceinline__ void store_r(uint4* r, int tid, const uint4& a0, const uint4& a1) {
-  const int c = tid & 7, rr = 2 * (tid >> 3);
-  r[r_index(rr, c)] = a0;
-  r[r_index(rr + 1, c)] = a1;
-}
-__device__ __forceinline__ void store_t(uint4* t, int tid, const uint4& a0, const uint4& a1) {
-  const int c = tid & 7, rr = 2 * (tid >> 3);
-  uint32_t words[8];
-  pack_pairs(a0, a1, words);
-  uint32_t* tw = (uint32_t*)t;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) tw[t_word(8 * c + j, rr)] = words[j];
+__device__ __forceinline__ bf16x8 words_bf16(const uint32_t (&w)[8], int half) {
+  return __builtin_bit_cast(bf16x8, uint4{w[4 * half], w[4 * half + 1], w[4 * half + 2], w[4 * half + 3]});
 }
 
-__device__ __forceinline__ bf16x8 slots_bf16(const f32x16& x, int half) {
-  const int e0 = 8 * half;
-  return __builtin_bit_cast(bf16x8, uint4{pack_bf16(x[e0], x[e0 + 1]), pack_bf16(x[e0 + 2], x[e0 + 3]),
-                                          pack_bf16(x[e0 + 4], x[e0 + 5]),
-                                          pack_bf16(x[e0 + 6], x[e0 + 7])});
-}
-
-// ---------------------------------------------------------------- dK, dV --
-__device__ void bwd_kv_unit(const AttnBwdArgs& a, BwdKVSmem* sm, int64_t unit) {
+// kKV: key unit (dK, dV) or query unit (dQ).
+template <bool kKV>
+__device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, uint32_t unit) {
+  constexpr int kIns = kKV ? 5 : 4;  // DMA instructions per tile and wave
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int li = lane & 31, lg = lane >> 5;
   int pp, b, h, tile;
   int64_t seg;
-  decode_unit(a.sched_kv, (uint32_t)unit, (int)a.H, &a.nseg, pp, b, h, seg, tile);
+  decode_unit(kKV ? a.sched_kv : a.sched_q, unit, (int)a.H, &a.nseg, pp, b, h, seg, tile);
   const int w = a.w, r = a.r, L = a.L;
   // Under a causal mask a key tile's work shrinks with its index: run low tiles first.
-  if (a.causal) tile = (L + kBwdT - 1) / kBwdT - 1 - tile;
+  if (kKV && a.causal) tile = (L + kBwdRows - 1) / kBwdRows - 1 - tile;
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const int64_t rstride = (int64_t)r * a.sn;
@@ -125,117 +100,287 @@ __device__ void bwd_kv_unit(const AttnBwdArgs& a, BwdKVSmem* sm, int64_t unit) {
   const __bf16* Kh = (const __bf16*)a.k + row_off;
   const __bf16* Vh = (const __bf16*)a.v + row_off;
   const __bf16* Dh = (const __bf16*)a.dout + row_off;
-  const int64_t bh = (int64_t)b * a.H + h;
-  const float* lse_h = a.lse + bh * a.N + base_row;      // stride r
-  const float* del_h = a.delta + bh * a.N + base_row;
+  const float2* ldh = a.ld + ((int64_t)b * a.H + h) * a.N + base_row;  // row stride r
   const float c = a.scale_log2;
 
-  const int k0 = tile * kBwdT;
-  const int kw0 = k0 + 32 * wave;
-  const int key = kw0 + li;
-  // K and V of this lane's key as B operands (d = 16ks + 8lg .. +8)
-  bf16x8 kop[4], vop[4];
+  // Owned rows: keys (key units) or queries (query units), 32 per wave.
+  const int own0 = tile * kBwdRows + 32 * wave;
+  const int own = own0 + li;
+  const bool wave_valid = own0 < L;
+  const __bf16* srcA = kKV ? Qh : Kh;   // streamed tensors
+  const __bf16* srcB = kKV ? Dh : Vh;
+  const __bf16* ownA = kKV ? Kh : Qh;   // owned tensors (B operands)
+  const __bf16* ownB = kKV ? Vh : Dh;
+  bf16x8 opa[4], opb[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    if (key < L) {
-      kop[ks] = *(const bf16x8*)(Kh + (int64_t)key * rstride + 16 * ks + 8 * lg);
-      vop[ks] = *(const bf16x8*)(Vh + (int64_t)key * rstride + 16 * ks + 8 * lg);
+    if (own < L) {
+      opa[ks] = *(const bf16x8*)(ownA + (int64_t)own * rstride + 16 * ks + 8 * lg);
+      opb[ks] = *(const bf16x8*)(ownB + (int64_t)own * rstride + 16 * ks + 8 * lg);
     } else {
-      kop[ks] = bf16x8{};
-      vop[ks] = bf16x8{};
+      opa[ks] = bf16x8{};
+      opb[ks] = bf16x8{};
     }
   }
-  f32x16 dk[2], dv[2];
-#pragma unroll
-  for (int db = 0; db < 2; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
-
-  const int nqt = (L + kBwdS - 1) / kBwdS;
-  const int qt0 = a.causal ? k0 / kBwdS : 0;
-  const bool wave_active = kw0 < L;
-
-  uint4 q0r, q1r, d0r, d1r;
-  float lse_r = 0.f, del_r = 0.f;
-  auto load = [&](int qt) {
-    const int r0 = qt * kBwdS;
-    load_pair(Qh, rstride, r0, L, tid, q0r, q1r);
-    load_pair(Dh, rstride, r0, L, tid, d0r, d1r);
-    if (tid < kBwdS) {
-      const int row = r0 + tid;
-      lse_r = row < L ? lse_h[(int64_t)row * r] * kLog2e : 0.f;
-      del_r = row < L ? del_h[(int64_t)row * r] : 0.f;
-    }
-  };
-  auto store = [&](int buf) {
-    store_r(sm[buf].q, tid, q0r, q1r);
-    store_t(sm[buf].qt, tid, q0r, q1r);
-    store_r(sm[buf].d, tid, d0r, d1r);
-    store_t(sm[buf].dt, tid, d0r, d1r);
-    if (tid < kBwdS) {
-      sm[buf].lse2[tid] = lse_r;
-      sm[buf].delta[tid] = del_r;
-    }
-  };
-
-  if (qt0 < nqt) {
-    load(qt0);
-    store(0);
+  float lse2_own = 0.f, d_own = 0.f;  // query units: this lane's query row
+  if (!kKV && own < L) {
+    const float2 x = ldh[(int64_t)own * r];
+    lse2_own = x.x;
+    d_own = x.y;
   }
-  __syncthreads();
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int buf = (qt - qt0) & 1;
-    if (qt + 1 < nqt) load(qt + 1);
-    const int q0 = qt * kBwdS;
-    const bool run = wave_active && (!a.causal || q0 + kBwdS > kw0);
-    if (run) {
-      const BwdKVSmem& s = sm[buf];
-      f32x16 S[2], dP[2];
+
+  // Streamed range: tiles t = 0..nt-1 start at row 64*(t_first + t); half h
+  // covers streamed rows s0(h) = 64*t_first + 32h .. +32.
+  int t_first, nt, h_lo, h_hi;
+  if (kKV) {
+    t_first = a.causal ? 2 * tile : 0;                 // queries >= the first owned key
+    nt = (L + kBwdTile - 1) / kBwdTile - t_first;
+    h_lo = a.causal ? wave : 0;                        // first half with a query >= own0
+    h_hi = (L - kBwdTile * t_first + 31) / 32;
+  } else {
+    t_first = 0;
+    const int kend = a.causal ? min(L, tile * kBwdRows + kBwdRows) : L;
+    nt = (kend + kBwdTile - 1) / kBwdTile;
+    h_lo = 0;
+    h_hi = a.causal ? min((L + 31) / 32, own0 / 32 + 1) : (L + 31) / 32;
+  }
+  auto active = [&](int hh) __attribute__((always_inline)) {
+    return wave_valid && hh >= h_lo && hh < h_hi;
+  };
+  auto need_mask = [&](int hh) __attribute__((always_inline)) {
+    const int s0 = kBwdTile * t_first + 32 * hh;
+    const bool diag = a.causal && (kKV ? own0 + 31 > s0 : s0 + 31 > own0);
+    return diag || (s0 + 32 > L) || (own0 + 32 > L);
+  };
+
+  // ---- HBM -> LDS: wave w fills rows [16w, 16w+16) of a tile, 8 rows per
+  // instruction; lane l lands at row 16w + 8i + l/8, chunk slot l%8, and loads
+  // the logical chunk that belongs there (u_swz depends on row % 16 only).
+  // Rows past the segment end load row L-1 (finite values, masked later).
+  const uint32_t rsb = (uint32_t)(rstride * 2);       // bytes between streamed rows
+  const uint32_t span = 63u * rsb + 128u;              // bytes a tile's rows cover
+  const int drow = 16 * wave + (lane >> 3);
+  uint32_t choff[2], voff[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) { S[qb] = f32x16{}; dP[qb] = f32x16{}; }
+  for (int i = 0; i < 2; ++i) {
+    choff[i] = 16u * (uint32_t)((lane & 7) ^ u_swz(8 * i + (lane >> 3)));
+    voff[i] = (uint32_t)(drow + 8 * i) * rsb + choff[i];
+  }
+  const uint32_t ld_voff = (uint32_t)(16 * wave + (lane >> 1)) * (uint32_t)(8 * r) + 4u * (lane & 1);
+  auto issue_tile = [&](int t, BwdStage* __restrict__ dst) __attribute__((always_inline)) {
+    const int trow0 = kBwdTile * (t_first + t);
+    const int lim = L - 1 - trow0;                      // last valid row of the tile
+    const __amdgpu_buffer_rsrc_t ra = buf_rsrc(srcA + (int64_t)trow0 * rstride, span);
+    const __amdgpu_buffer_rsrc_t rb = buf_rsrc(srcB + (int64_t)trow0 * rstride, span);
+    uint32_t vo[2] = {voff[0], voff[1]};
+    if (lim < kBwdTile - 1) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int i = 0; i < 2; ++i) vo[i] = (uint32_t)min(drow + 8 * i, lim) * rsb + choff[i];
+    }
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const bf16x8 qa = *(const bf16x8*)&s.q[r_index(32 * qb + li, 2 * ks + lg)];
-          const bf16x8 da = *(const bf16x8*)&s.d[r_index(32 * qb + li, 2 * ks + lg)];
-          S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[ks], S[qb], 0, 0, 0);
-          dP[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vop[ks], dP[qb], 0, 0, 0);
-        }
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(dst->a + 8 * (16 * wave + 8 * i)), 16, vo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(dst->b + 8 * (16 * wave + 8 * i)), 16, vo[i], 0, 0, 0);
+    }
+    if (kKV) {
+      // (LSE*log2e, D) of rows 16w .. 16w+15: lanes 0..31 load one float each.
+      const __amdgpu_buffer_rsrc_t rl = buf_rsrc(ldh + (int64_t)trow0 * r, 63u * (uint32_t)(8 * r) + 8u);
+      uint32_t lo = ld_voff;
+      if (lim < kBwdTile - 1)
+        lo = (uint32_t)min(16 * wave + (lane >> 1), lim) * (uint32_t)(8 * r) + 4u * (lane & 1);
+      if (lane < 32)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)((float*)dst->ld + 32 * wave), 4, lo, 0, 0, 0);
+    }
+  };
+
+  // ---- per-lane LDS read offsets ----------------------------------------------
+  int roff[4];                 // row-wise operand: row 32*blk + li, chunk 2ks + lg (+ blk*4096)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_offset(lane, 0, ks);
+  int tlo[2], thi[2];          // transposed operand of head-dim block db (+ kk*2048)
+#pragma unroll
+  for (int db = 0; db < 2; ++db) tr_offsets(lane, db, tlo[db], thi[db]);
+
+  // ---- accumulators -----------------------------------------------------------
+  f32x16 acc0[2], acc1[2];     // key units: dK^T[db], dV^T[db]; query units: dQ^T[db] in acc0
+#pragma unroll
+  for (int db = 0; db < 2; ++db) { acc0[db] = f32x16{}; acc1[db] = f32x16{}; }
+
+  // ---- pipeline stages ------------------------------------------------------
+  // S and dP of half hh (blk = hh & 1 within its tile).
+  auto stage_sd = [&](const BwdStage* __restrict__ st, int blk, f32x16& S, f32x16& P) __attribute__((always_inline)) {
+    S = f32x16{};
+    P = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 xa = lds_read_b128((const lds_u4*)st->a, blk * 4096 + roff[ks]);
+      const bf16x8 xb = lds_read_b128((const lds_u4*)st->b, blk * 4096 + roff[ks]);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, opa[ks], S, 0, 0, 0);
+      P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, opb[ks], P, 0, 0, 0);
+    }
+  };
+  // P and dS of half hh from its S and dP, packed to bf16 operand words.
+  auto stage_valu = [&](int hh, const BwdStage* __restrict__ st, int blk, const f32x16& S,
+                        const f32x16& P, bool masked, uint32_t (&pw)[8], uint32_t (&sw)[8]) __attribute__((always_inline)) {
+    const int s0 = kBwdTile * t_first + 32 * hh;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float l2[4], dd[4];
+      if (kKV) {
+        // rows 32*blk + 8g + 4lg + i of the tile: four (LSE2, D) pairs
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+        const lds_char* base = (const lds_char*)st->ld + 8 * (32 * blk + 8 * g + 4 * lg);
+        const f32x4 x0 = *(const lds_f32x4*)base;
+        const f32x4 x1 = *(const lds_f32x4*)(base + 16);
+        l2[0] = x0[0]; dd[0] = x0[1]; l2[1] = x0[2]; dd[1] = x0[3];
+        l2[2] = x1[0]; dd[2] = x1[1]; l2[3] = x1[2]; dd[3] = x1[3];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { l2[i] = lse2_own; dd[i] = d_own; }
       }
-      const bool need_mask = (q0 + kBwdS > L) || (kw0 + 32 > L) || (a.causal && q0 < kw0 + 32);
+      float pv[4], dv[4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int ql = 32 * qb + (e >> 2) * 8 + lg * 4 + (e & 3);
-          const float4 ld = float4{s.lse2[ql], s.delta[ql], 0.f, 0.f};
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][e], c, -ld.x));
-          if (need_mask) {
-            const int q = q0 + ql;
-            if (q >= L || key >= L || (a.causal && key > q)) pv = 0.f;
-          }
-          S[qb][e] = pv;
-          dP[qb][e] = pv * (dP[qb][e] - ld.y);
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * g + i;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, -l2[i]));
+        if (masked) {
+          const int srow = s0 + 8 * g + 4 * lg + i;
+          const bool dead = kKV ? (srow >= L || own >= L || (a.causal && own > srow))
+                                : (srow >= L || own >= L || (a.causal && srow > own));
+          if (dead) p = 0.f;
         }
+        pv[i] = p;
+        dv[i] = p * (P[e] - dd[i]);
       }
+      if (kKV) {
+        pw[2 * g] = pack_bf16(pv[0], pv[1]);
+        pw[2 * g + 1] = pack_bf16(pv[2], pv[3]);
+      }
+      sw[2 * g] = pack_bf16(dv[0], dv[1]);
+      sw[2 * g + 1] = pack_bf16(dv[2], dv[3]);
+    }
+  };
+  // Gradient products of half hh: key units dV^T += dO^T P, dK^T += Q^T dS;
+  // query units dQ^T += K^T dS^T.
+  auto stage_grad = [&](const BwdStage* __restrict__ st, int blk, const uint32_t (&pw)[8],
+                        const uint32_t (&sw)[8]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 pb = slots_bf16(S[kk >> 1], kk & 1);
-        const bf16x8 sb = slots_bf16(dP[kk >> 1], kk & 1);
+    for (int half = 0; half < 2; ++half) {
+      const int kko = (2 * blk + half) * 2048;
+      const bf16x8 sb = words_bf16(sw, half);
+      if (kKV) {
+        const bf16x8 pb = words_bf16(pw, half);
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const bf16x8 dta = *(const bf16x8*)&s.dt[t_chunk(32 * db + li, kk, lg)];
-          const bf16x8 qta = *(const bf16x8*)&s.qt[t_chunk(32 * db + li, kk, lg)];
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dta, pb, dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, sb, dk[db], 0, 0, 0);
+          const bf16x8 dta = lds_read_tr8((const lds_u4*)st->b, tlo[db] + kko, thi[db] + kko);
+          const bf16x8 qta = lds_read_tr8((const lds_u4*)st->a, tlo[db] + kko, thi[db] + kko);
+          acc1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dta, pb, acc1[db], 0, 0, 0);
+          acc0[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, sb, acc0[db], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const bf16x8 kta = lds_read_tr8((const lds_u4*)st->a, tlo[db] + kko, thi[db] + kko);
+          acc0[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, sb, acc0[db], 0, 0, 0);
         }
       }
     }
-    if (qt + 1 < nqt) store(buf ^ 1);
-    __syncthreads();
-  }
+  };
 
-  if (!wave_active || key >= L) return;
-  const int64_t n = base_row + (int64_t)key * r;
+  f32x16 sx, px, sy, py;                       // S, dP of the even (x) / odd (y) half in flight
+  uint32_t pwx[8], swx[8], pwy[8], swy[8];     // packed P, dS of the even / odd half
+
+  // One phase: gradient products of hh-1 (stage sg, block 1-blk), S/dP of
+  // hh+1 (stage ss, block 1-blk), P/dS of hh (stage sv, block blk).  In the
+  // steady state (all three halves active, no mask) they run in one block:
+  //   query units: all three interleaved (S/dP double-buffered);
+  //   key units:   gradient MFMAs interleaved with the VALU, then S/dP of hh+1
+  //                into the registers the VALU just consumed (their register
+  //                budget has no room for a second S/dP set).
+  // Stages that do not run mark their outputs dead, so that the register
+  // allocator need not keep the stale values alive across the phase.
+#define DLA_DEAD(x) x = __builtin_nondeterministic_value(x)
+#define DLA_BWD_PHASE(hh, blk, sg, ss, sv, S_cur, P_cur, S_nxt, P_nxt, pw_cur, sw_cur, pw_prv, sw_prv) \
+  do {                                                                                           \
+    const bool a_prev = active((hh) - 1), a_cur = active(hh), a_next = active((hh) + 1);        \
+    const bool msk = need_mask(hh);                                                              \
+    if (!kKV && a_prev && a_cur && a_next && !msk) {                                             \
+      stage_grad(sg, 1 - (blk), pw_prv, sw_prv);                                                 \
+      stage_sd(ss, 1 - (blk), S_nxt, P_nxt);                                                     \
+      stage_valu(hh, sv, blk, S_cur, P_cur, false, pw_cur, sw_cur);                              \
+      DLA_INTERLEAVE(12, 6);                                                                     \
+    } else {                                                                                     \
+      if (kKV && a_prev && a_cur && !msk) {                                                      \
+        stage_grad(sg, 1 - (blk), pw_prv, sw_prv);                                               \
+        stage_valu(hh, sv, blk, S_cur, P_cur, false, pw_cur, sw_cur);                            \
+        DLA_INTERLEAVE(8, 10);                                                                   \
+      } else {                                                                                   \
+        if (a_prev) stage_grad(sg, 1 - (blk), pw_prv, sw_prv);                                   \
+        if (a_cur) {                                                                             \
+          if (msk) stage_valu(hh, sv, blk, S_cur, P_cur, true, pw_cur, sw_cur);                  \
+          else stage_valu(hh, sv, blk, S_cur, P_cur, false, pw_cur, sw_cur);                     \
+        } else {                                                                                 \
+          _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { DLA_DEAD(pw_cur[i_]); DLA_DEAD(sw_cur[i_]); } \
+        }                                                                                        \
+      }                                                                                          \
+      if (a_next) {                                                                              \
+        stage_sd(ss, 1 - (blk), S_nxt, P_nxt);                                                   \
+      } else {                                                                                   \
+        DLA_DEAD(S_nxt);                                                                         \
+        DLA_DEAD(P_nxt);                                                                         \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+
+  // Ring step j: phase 2j reads tiles j-1 and j; then wait until tile j+1
+  // is in LDS (tile j+2 may stay in flight), synchronise, refill the stage of
+  // tile j-1 with tile j+3, and run phase 2j+1 on tiles j and j+1.  The
+  // distinct restrict pointers tell the compiler that the DMA target is not
+  // read after the refill, so it adds no waits of its own.
+  auto ring_step = [&](int j, const BwdStage* __restrict__ sp, const BwdStage* __restrict__ sc,
+                       const BwdStage* __restrict__ sn, BwdStage* __restrict__ si) __attribute__((always_inline)) {
+    if (kKV) DLA_BWD_PHASE(2 * j, 0, sp, sc, sc, sx, px, sx, px, pwx, swx, pwy, swy);
+    else DLA_BWD_PHASE(2 * j, 0, sp, sc, sc, sx, px, sy, py, pwx, swx, pwy, swy);
+    if (j + 2 < nt) {
+      if (kKV) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + 3 < nt) issue_tile(j + 3, si);
+    if (kKV) DLA_BWD_PHASE(2 * j + 1, 1, sc, sn, sc, sx, px, sx, px, pwy, swy, pwx, swx);
+    else DLA_BWD_PHASE(2 * j + 1, 1, sc, sn, sc, sy, py, sx, px, pwy, swy, pwx, swx);
+  };
+
+  // Prologue: tiles 0..2 in flight, wait for tile 0, S/dP of half 0.
+  issue_tile(0, &ring[0]);
+  if (nt > 1) issue_tile(1, &ring[1]);
+  if (nt > 2) issue_tile(2, &ring[2]);
+  if (nt > 2) {
+    if (kKV) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else if (nt > 1) {
+    if (kKV) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (active(0)) stage_sd(&ring[0], 0, sx, px);
+
+  for (int j = 0; j < nt; ++j)
+    ring_step(j, &ring[(j + 3) & 3], &ring[j & 3], &ring[(j + 1) & 3], &ring[(j + 3) & 3]);
+  // Drain: gradient products of the last half.
+  if (active(2 * nt - 1)) stage_grad(&ring[(nt - 1) & 3], 1, pwy, swy);
+#undef DLA_BWD_PHASE
+#undef DLA_DEAD
+  (void)kIns;
+
+  if (!wave_valid || own >= L) return;
+  const int64_t n = base_row + (int64_t)own * r;
   const int st = cover_state(a, n, h);
   const int64_t acc_off = ((int64_t)b * a.N + n) * a.H * kD + (int64_t)h * kD;
   const int64_t out_off = head_off + n * a.sn;
@@ -244,145 +389,27 @@ __device__ void bwd_kv_unit(const AttnBwdArgs& a, BwdKVSmem* sm, int64_t unit) {
 #pragma unroll
     for (int eg = 0; eg < 4; ++eg) {
       const int d0 = 32 * db + 8 * eg + 4 * lg;
-      const f32x16& kv = dk[db];
-      const f32x16& vv = dv[db];
-      emit4(st, a.dk_acc + acc_off, (__bf16*)a.dk + out_off, d0, a.scale * kv[4 * eg],
-            a.scale * kv[4 * eg + 1], a.scale * kv[4 * eg + 2], a.scale * kv[4 * eg + 3]);
-      emit4(st, a.dv_acc + acc_off, (__bf16*)a.dv + out_off, d0, vv[4 * eg], vv[4 * eg + 1],
-            vv[4 * eg + 2], vv[4 * eg + 3]);
-    }
-}
-
-// --------------------------------------------------------------------- dQ --
-__device__ void bwd_q_unit(const AttnBwdArgs& a, BwdQSmem* sm, int64_t unit) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 31, lg = lane >> 5;
-  int pp, b, h, tile;
-  int64_t seg;
-  decode_unit(a.sched_q, (uint32_t)unit, (int)a.H, &a.nseg, pp, b, h, seg, tile);
-  const int w = a.w, r = a.r, L = a.L;
-  const int64_t base_row = seg_base_row(seg, w, r, h);
-  const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const int64_t rstride = (int64_t)r * a.sn;
-  const int64_t row_off = head_off + base_row * a.sn;
-  const __bf16* Qh = (const __bf16*)a.q + row_off;
-  const __bf16* Kh = (const __bf16*)a.k + row_off;
-  const __bf16* Vh = (const __bf16*)a.v + row_off;
-  const __bf16* Dh = (const __bf16*)a.dout + row_off;
-  const int64_t bh = (int64_t)b * a.H + h;
-  const float c = a.scale_log2;
-
-  const int q0 = tile * kBwdT;
-  const int qw0 = q0 + 32 * wave;
-  const int q = qw0 + li;
-  const bool qvalid = q < L;
-  bf16x8 qop[4], dop[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (qvalid) {
-      qop[ks] = *(const bf16x8*)(Qh + (int64_t)q * rstride + 16 * ks + 8 * lg);
-      dop[ks] = *(const bf16x8*)(Dh + (int64_t)q * rstride + 16 * ks + 8 * lg);
-    } else {
-      qop[ks] = bf16x8{};
-      dop[ks] = bf16x8{};
-    }
-  }
-  const float lse2 = qvalid ? a.lse[bh * a.N + base_row + (int64_t)q * r] * kLog2e : 0.f;
-  const float del = qvalid ? a.delta[bh * a.N + base_row + (int64_t)q * r] : 0.f;
-  f32x16 dq[2];
-  dq[0] = f32x16{};
-  dq[1] = f32x16{};
-
-  const int kend = a.causal ? min(L, q0 + kBwdT) : L;
-  const int nkt = (kend + kBwdS - 1) / kBwdS;
-  const bool wave_active = qw0 < L;
-
-  uint4 k0r, k1r, v0r, v1r;
-  auto load = [&](int kt) {
-    load_pair(Kh, rstride, kt * kBwdS, L, tid, k0r, k1r);
-    load_pair(Vh, rstride, kt * kBwdS, L, tid, v0r, v1r);
-  };
-  auto store = [&](int buf) {
-    store_r(sm[buf].k, tid, k0r, k1r);
-    store_t(sm[buf].kt, tid, k0r, k1r);
-    store_r(sm[buf].v, tid, v0r, v1r);
-  };
-  if (nkt > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) load(kt + 1);
-    const int kb0 = kt * kBwdS;
-    const bool run = wave_active && (!a.causal || kb0 < qw0 + 32);
-    if (run) {
-      const BwdQSmem& s = sm[buf];
-      f32x16 S[2], dP[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) { S[kb] = f32x16{}; dP[kb] = f32x16{}; }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *(const bf16x8*)&s.k[r_index(32 * kb + li, 2 * ks + lg)];
-          const bf16x8 va = *(const bf16x8*)&s.v[r_index(32 * kb + li, 2 * ks + lg)];
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[ks], S[kb], 0, 0, 0);
-          dP[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dop[ks], dP[kb], 0, 0, 0);
-        }
+      const f32x16& x = acc0[db];
+      if (kKV) {
+        const f32x16& y = acc1[db];
+        emit4(st, a.dk_acc + acc_off, (__bf16*)a.dk + out_off, d0, a.scale * x[4 * eg],
+              a.scale * x[4 * eg + 1], a.scale * x[4 * eg + 2], a.scale * x[4 * eg + 3]);
+        emit4(st, a.dv_acc + acc_off, (__bf16*)a.dv + out_off, d0, y[4 * eg], y[4 * eg + 1],
+              y[4 * eg + 2], y[4 * eg + 3]);
+      } else {
+        emit4(st, a.dq_acc + acc_off, (__bf16*)a.dq + out_off, d0, a.scale * x[4 * eg],
+              a.scale * x[4 * eg + 1], a.scale * x[4 * eg + 2], a.scale * x[4 * eg + 3]);
       }
-      const bool need_mask = (kb0 + kBwdS > L) || !qvalid || (a.causal && kb0 + kBwdS > qw0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], c, -lse2));
-          if (need_mask) {
-            const int kk = kb0 + 32 * kb + (e >> 2) * 8 + lg * 4 + (e & 3);
-            if (!qvalid || kk >= L || (a.causal && kk > q)) pv = 0.f;
-          }
-          dP[kb][e] = pv * (dP[kb][e] - del);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 sb = slots_bf16(dP[kk >> 1], kk & 1);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const bf16x8 kta = *(const bf16x8*)&s.kt[t_chunk(32 * db + li, kk, lg)];
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, sb, dq[db], 0, 0, 0);
-        }
-      }
-    }
-    if (kt + 1 < nkt) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (!qvalid) return;
-  const int64_t n = base_row + (int64_t)q * r;
-  const int st = cover_state(a, n, h);
-  const int64_t acc_off = ((int64_t)b * a.N + n) * a.H * kD + (int64_t)h * kD;
-  const int64_t out_off = head_off + n * a.sn;
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int eg = 0; eg < 4; ++eg) {
-      const int d0 = 32 * db + 8 * eg + 4 * lg;
-      const f32x16& x = dq[db];
-      emit4(st, a.dq_acc + acc_off, (__bf16*)a.dq + out_off, d0, a.scale * x[4 * eg],
-            a.scale * x[4 * eg + 1], a.scale * x[4 * eg + 2], a.scale * x[4 * eg + 3]);
     }
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bwd_bf16_kernel(const AttnBwdArgs a) {
-  __shared__ BwdSmem sm;
-  const int64_t u = blockIdx.x;
-  if (u < a.sched_kv.total) {
-    bwd_kv_unit(a, sm.kv, u);
+  __shared__ BwdStage ring[kBwdStages];
+  const uint32_t u = blockIdx.x;
+  if (u < (uint32_t)a.sched_kv.total) {
+    bwd_unit<true>(a, ring, u);
   } else {
-    bwd_q_unit(a, sm.qs, u - a.sched_kv.total);
+    bwd_unit<false>(a, ring, u - (uint32_t)a.sched_kv.total);
   }
 }
 

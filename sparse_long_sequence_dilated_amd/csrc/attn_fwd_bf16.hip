@@ -47,15 +47,6 @@ struct __align__(16) FwdStage {
 
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
 
-// Instruction-interleaving hints for one phase: n MFMAs, each followed by v VALU ops.
-#define DLA_INTERLEAVE(n, v)                                   \
-  do {                                                         \
-    _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {       \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       \
-      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);     \
-    }                                                          \
-  } while (0)
-
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs a) {
   __shared__ FwdStage ring[kStages];
   const int tid = threadIdx.x;

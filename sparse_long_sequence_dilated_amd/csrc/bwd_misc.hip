@@ -1,5 +1,7 @@
-// Backward preprocessing: D = rowsum(dO * O) per (batch, head, row), and zero
-// gradients for rows that no pattern keeps (their output is the constant 0).
+// Backward preprocessing: D = rowsum(dO * O) per (batch, head, row), stored
+// next to the combined LSE (pre-multiplied by log2 e) so that the attention
+// backward fetches both with one 8-byte load per row; and zero gradients for
+// rows that no pattern keeps (their output is the constant 0).
 // Eight lanes per (b, n, h) row, eight d values each; rows walked in
 // [B, N, H] order so that O and dO are read contiguously.  HBM bound.
 #include "dla_device.h"
@@ -53,7 +55,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdPrepArgs a) {
   s += __shfl_xor(s, 1);
   s += __shfl_xor(s, 2);
   s += __shfl_xor(s, 4);
-  if (c == 0) a.delta[(b * a.H + h) * a.N + n] = s;
+  if (c == 0) {
+    const int64_t i = (b * a.H + h) * a.N + n;
+    a.ld[i] = float2{a.lse[i] * kLog2e, s};
+  }
   if (a.zero_uncovered) {
     bool kept = false;
     for (int p = 0; p < a.P; ++p) kept |= (n % a.r_all[p]) == (h % a.r_all[p]);

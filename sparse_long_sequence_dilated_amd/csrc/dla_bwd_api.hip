@@ -38,12 +38,13 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
     return fail(DLA_E_UNSUPPORTED, "the backward pass is implemented for bf16 tensors");
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
-  float* delta = (float*)(wsb + pl.delta_off);
+  float2* ld = (float2*)(wsb + pl.delta_off);
 
   BwdPrepArgs pa{};
   pa.o = o;
   pa.dout = dout;
-  pa.delta = delta;
+  pa.lse = lse;
+  pa.ld = ld;
   pa.dq = dq;
   pa.dk = dk;
   pa.dv = dv;
@@ -69,8 +70,7 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
   a.k = k;
   a.v = v;
   a.dout = dout;
-  a.lse = lse;
-  a.delta = delta;
+  a.ld = ld;
   a.dq_acc = (float*)(wsb + pl.dq_off);
   a.dk_acc = (float*)(wsb + pl.dk_off);
   a.dv_acc = (float*)(wsb + pl.dv_off);

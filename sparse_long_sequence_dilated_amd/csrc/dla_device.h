@@ -135,32 +135,48 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ bf16x8 lds_read_b128(const lds_u4* base, int byte_off) {
   return __builtin_bit_cast(bf16x8, *(const lds_u4*)((const lds_char*)base + byte_off));
 }
-// MFMA operand with 8 consecutive sequence rows of one head dimension from a
-// row-major u-swizzled tile: two transposed 8-byte reads (rows +0..3 and +8..11
-// relative to the lane's address), matching the k-slot order of an operand
-// that comes from a 32x32 accumulator.
-__device__ __forceinline__ bf16x8 lds_read_tr8(const lds_u4* base, int byte_off) {
-  const lds_char* p = (const lds_char*)base + byte_off;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * 128));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+// MFMA operand with 8 sequence rows of one head dimension from a row-major
+// u-swizzled tile: two transposed 8-byte reads, rows +0..3 at byte offset
+// `lo` and rows +8..11 at `hi`, matching the k-slot order of an operand that
+// comes from a 32x32 accumulator.
+__device__ __forceinline__ bf16x8 lds_read_tr8(const lds_u4* base, int lo, int hi) {
+  const lds_char* p = (const lds_char*)base;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + lo));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-// Per-lane byte offset of lds_read_tr8 for head-dimension block db (32 dims)
-// and 16-row k-step kk of a 64-row tile: lane l = 16m + t supplies row
-// 16kk + 8*half + 4*(m/2) + t/4 and dims 32db + 16(m%2) + 4(t%4) .. +4, and
-// receives rows (16kk + 4*(l/32)) + {0..3, 8..11} of head dim 32db + l%32.
-// The k-step enters as + kk*16*128 (u_swz depends on row % 16 only).
-__device__ __forceinline__ int tr_offset(int lane, int db) {
+// Per-lane byte offsets (lo, hi) of lds_read_tr8 for head-dimension block db
+// (32 dims) of the 16-row k-step at rows 0..15 of a tile; k-step kk adds
+// kk * 16 * 128 to both (u_swz depends on row % 16 only).  Lane l = 16m + t
+// supplies row 4*(m/2) + t/4 (lo) or that + 8 (hi) and dims 32db + 16(m%2) +
+// 4(t%4) .. +4, and receives rows 4*(l/32) + {0..3, 8..11} of head dim
+// 32db + l%32.  Row + 8 flips bit 1 of the swizzle, i.e. bit 5 of the offset.
+__device__ __forceinline__ void tr_offsets(int lane, int db, int& lo, int& hi) {
   const int t = lane & 15, m = lane >> 4;
   const int row = 4 * (m >> 1) + (t >> 2);
   const int chunk = 4 * db + 2 * (m & 1) + ((t & 3) >> 1);
-  return row * 128 + ((chunk ^ u_swz(row)) << 4) + 8 * (t & 1);
+  lo = row * 128 + ((chunk ^ u_swz(row)) << 4) + 8 * (t & 1);
+  hi = (lo ^ 32) + 8 * 128;
 }
 // Per-lane byte offset of the row-wise operand read: row 32*blk + (lane%32),
 // logical chunk 2*ks + lane/32.
 __device__ __forceinline__ int row_offset(int lane, int blk, int ks) {
   const int row = 32 * blk + (lane & 31);
   return row * 128 + (((2 * ks + (lane >> 5)) ^ u_swz(row)) << 4);
+}
+
+// Instruction-interleaving hints for one phase: n MFMAs, each followed by v VALU ops.
+#define DLA_INTERLEAVE(n, v)                                   \
+  do {                                                         \
+    _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       \
+      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);     \
+    }                                                          \
+  } while (0)
+
+// Raw buffer resource over [base, base + bytes) (gfx9 dword3 for untyped access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Pack two rows' 16-byte chunks (8 bf16 each, same d range) into the 8 words

@@ -55,8 +55,7 @@ struct AttnBwdArgs {
   const void* k;
   const void* v;
   const void* dout;
-  const float* lse;        // combined LSE [B,H,N]
-  const float* delta;      // D = rowsum(dO*O) [B,H,N]
+  const float2* ld;        // (combined LSE * log2 e, D = rowsum(dO*O)) [B,H,N]
   float* dq_acc;           // fp32 [B,N,H,D] accumulators (contiguous)
   float* dk_acc;
   float* dv_acc;
@@ -79,7 +78,8 @@ struct AttnBwdArgs {
 struct BwdPrepArgs {
   const void* o;
   const void* dout;
-  float* delta;
+  const float* lse;        // combined LSE [B,H,N]
+  float2* ld;              // out: (LSE * log2 e, D) [B,H,N]
   void* dq;
   void* dk;
   void* dv;

@@ -71,6 +71,10 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan) {
                              (long long)p.N);
     if (p.N % w) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d does not divide N=%lld", i, w,
                              (long long)p.N);
+    // The backward streams 64 dilated rows per tile through one 32-bit
+    // buffer offset range.
+    if ((int64_t)64 * r * shape->stride_n * (shape->dtype == DLA_F32 ? 4 : 2) + 128 > INT32_MAX)
+      return fail(DLA_E_UNSUPPORTED, "pattern %d: 64 dilated rows span more than 2 GiB", i);
     p.w[i] = w;
     p.r[i] = r;
     p.L[i] = w / r;
@@ -99,7 +103,7 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan) {
   const size_t rows_all = (size_t)p.B * p.N * p.H;
   off = 0;
   p.delta_off = off;
-  off = align_up(off + rows_all * sizeof(float), 256);
+  off = align_up(off + rows_all * 2 * sizeof(float), 256);
   p.dq_off = off;
   off = align_up(off + rows_all * kD * sizeof(float), 256);
   p.dk_off = off;
@@ -108,12 +112,21 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan) {
   off = align_up(off + rows_all * kD * sizeof(float), 256);
   p.ws_bwd = off;
 
+  // Useful (query, key) pairs; a count beyond int64 is refused.
   int64_t pairs = 0;
+  bool ovf = false;
   for (int i = 0; i < p.P; ++i) {
     const int64_t L = p.L[i];
-    pairs += p.nseg[i] * (p.causal ? L * (L + 1) / 2 : L * L);
+    int64_t per = 0, seg_pairs = 0;
+    ovf |= __builtin_mul_overflow(L, p.causal ? L + 1 : L, &per);
+    if (p.causal) per /= 2;
+    ovf |= __builtin_mul_overflow(p.nseg[i], per, &seg_pairs);
+    ovf |= __builtin_add_overflow(pairs, seg_pairs, &pairs);
   }
-  p.pairs = pairs * p.B * p.H;
+  ovf |= __builtin_mul_overflow(pairs, p.B, &pairs);
+  ovf |= __builtin_mul_overflow(pairs, p.H, &pairs);
+  if (ovf) return fail(DLA_E_UNSUPPORTED, "the number of attention pairs exceeds 2^63");
+  p.pairs = pairs;
   return DLA_OK;
 }
 

@@ -45,7 +45,8 @@ struct Plan {
   size_t part_o_off[kMaxP];
   size_t part_lse_off[kMaxP];
   size_t ws_fwd;
-  // backward workspace: D = rowsum(dO*O) [B,H,N] fp32, fp32 accumulators [B,N,H,D]
+  // backward workspace: (LSE * log2 e, D = rowsum(dO*O)) [B,H,N] float pairs,
+  // fp32 accumulators [B,N,H,D]
   size_t delta_off, dq_off, dk_off, dv_off;
   size_t ws_bwd;
   int64_t pairs;

@@ -106,7 +106,7 @@ def test_workspace_sizes_follow_closed_forms(name):
         rows = wl.B * wl.H * (wl.N // r)
         exp_f += _align(rows * 64 * eb) + _align(rows * 4)
     rows = wl.B * wl.N * wl.H
-    exp_b = _align(rows * 4) + 3 * _align(rows * 64 * 4)
+    exp_b = _align(rows * 8) + 3 * _align(rows * 64 * 4)
     assert (ws_f, ws_b) == (exp_f, exp_b)
 
 
@@ -159,6 +159,11 @@ int main(void) {
   /* huge problem: sizes must not overflow */
   s.B = 64; s.N = 1 << 30; s.H = 64; s.stride_b = (int64_t)s.N * 64 * 64; s.stride_n = 64 * 64;
   pats[0].w = 1 << 30; pats[0].r = 1 << 19; d.num_patterns = 1;
+  /* 64 dilated rows of r = 2^19 and 8 KB each span more than 2 GiB: refused */
+  bad += expect(dla_plan_check(&d, &s, &wf, &wb), DLA_E_UNSUPPORTED, "huge span");
+  pats[0].r = 1 << 4;   /* 2^26-row segments: 2^64 pairs, refused */
+  bad += expect(dla_plan_check(&d, &s, &wf, &wb), DLA_E_UNSUPPORTED, "huge pairs");
+  pats[0].r = 1 << 10;
   bad += expect(dla_plan_check(&d, &s, &wf, &wb), DLA_OK, "huge");
   if (wb < (size_t)64 * (1u << 30) * 64 * 64 * 4 * 3) { printf("FAIL huge ws %zu\n", wb); bad++; }
   printf(bad ? "FAILED %d\n" : "ALL OK\n", bad);
