@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "attn_bwd": ["attn_bwd_bf16.hip", "dla_device.h"],
     "combine": ["combine.hip", "dla_device.h"],
     "bwd_prep": ["bwd_misc.hip", "dla_device.h"],
+    "bwd_finalize": ["bwd_misc.hip", "dla_device.h"],
 }
 
 
@@ -69,6 +70,17 @@ def family_work(family, wl, pairs):
     rows = wl.B * wl.N * wl.H
     if family == "bwd_prep":
         return rows * (2 * D * 2 + 4), "byte", "hbm"    # read O, dO (bf16), write D (fp32)
+    if family == "bwd_finalize":
+        # rows kept by k >= 2 patterns: read k fp32 partial rows of dQ, dK, dV,
+        # write the three bf16 gradient rows
+        period = math.lcm(*[r for _, r in wl.patterns])
+        total = 0
+        for h in range(wl.H):
+            for n_mod in range(period):
+                kept = sum(1 for w, r in wl.patterns if n_mod % r == h % r)
+                if kept >= 2:
+                    total += 3 * (kept * D * 4 + D * 2) * (wl.N // period)
+        return total * wl.B, "byte", "hbm"
     if family == "combine":
         # rows kept by the primary pattern and >= 1 other: read O, LSE and each
         # other pattern's partial (O_p bf16, LSE_p fp32); write O, LSE
@@ -110,7 +122,7 @@ def time_steps(step, steps, warmup):
     t1 = time.perf_counter()
     dla.timing_enable(False)
     fams = {}
-    for fam in ("attn_fwd", "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd"):
+    for fam in ("attn_fwd", "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd", "bwd_finalize"):
         n, ms = dla.timing_collect(fam)
         if n:
             fams[fam] = (n, ms)

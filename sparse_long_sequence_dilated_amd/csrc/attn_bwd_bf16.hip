@@ -9,7 +9,7 @@
 // inside each sparsified segment (gptget.net LongNet summary, section 方法论),
 // with rows gathered by the same strided address generator as the forward.
 //
-// One launch per pattern holds two kinds of workgroups (4 waves each):
+// One launch covers all patterns with two kinds of workgroups (4 waves each):
 //   * key units own 128 keys (32 per wave), stream the segment's query rows
 //     (Q, dO, and the (LSE, D) pairs) and accumulate dK^T = Q^T dS and
 //     dV^T = dO^T P in registers;
@@ -27,10 +27,10 @@
 // pipeline: phase h issues the MFMAs of half h+1 (S, dP) and of half h-1 (the
 // gradient products) while the VALU computes P and dS of half h.
 //
-// Patterns run one launch after another.  Per output row the epilogue looks
-// up which other patterns keep that row: the first pattern to touch it writes
-// the fp32 accumulator, later ones add to it, and the last one adds and writes
-// the rounded gradient; a row kept by one pattern only is written directly.
+// Per output row the epilogue counts the patterns that keep it: a row kept by
+// this pattern alone gets its rounded gradient directly, a row kept by several
+// gets this pattern's fp32 partial in the pattern's own sparse-order buffer
+// (write-once, contiguous rows), and a finalize pass sums the partials.
 #include "dla_device.h"
 
 namespace dla {
@@ -45,33 +45,14 @@ struct __align__(16) BwdStage {
   float2 ld[kBwdTile];     // key units: (LSE * log2 e, D) of the tile's rows
 };
 
-// bit 0: a pattern processed earlier keeps row n of head h; bit 1: a later one does.
-__device__ __forceinline__ int cover_state(const AttnBwdArgs& a, int64_t n, int h) {
-  int st = 0;
-  const int my = a.rank[a.p];
+// Number of patterns that keep row n of head h (n = h mod r for each).
+__device__ __forceinline__ int kept_count(const AttnBwdArgs& a, int n, int h) {
+  int c = 0;
   for (int i = 0; i < a.P; ++i) {
-    if (i == a.p) continue;
-    const int ri = a.r_all[i];
-    if ((n % ri) != (h % ri)) continue;
-    st |= (a.rank[i] < my) ? 1 : 2;
+    const int ri = a.r[i];
+    c += (ri & (ri - 1)) == 0 ? (((n ^ h) & (ri - 1)) == 0) : ((n % ri) == (h % ri));
   }
-  return st;
-}
-
-// Write 4 consecutive gradient values of row `n` at d0 following the
-// first/middle/last rule above.
-__device__ __forceinline__ void emit4(int st, float* acc_row, __bf16* out_row, int d0, float x0,
-                                      float x1, float x2, float x3) {
-  float4 v = float4{x0, x1, x2, x3};
-  if (st & 1) {
-    const float4 o = *(const float4*)(acc_row + d0);
-    v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-  }
-  if (st & 2) {
-    *(float4*)(acc_row + d0) = v;
-  } else {
-    *(uint2*)(out_row + d0) = uint2{pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)};
-  }
+  return c;
 }
 
 __device__ __forceinline__ bf16x8 words_bf16(const uint32_t (&w)[8], int half) {
@@ -80,18 +61,14 @@ __device__ __forceinline__ bf16x8 words_bf16(const uint32_t (&w)[8], int half) {
 
 // kKV: key unit (dK, dV) or query unit (dQ).
 template <bool kKV>
-__device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, uint32_t unit) {
+__device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, int p, int b, int h,
+                                         int64_t seg, int tile) {
   constexpr int kIns = kKV ? 5 : 4;  // DMA instructions per tile and wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int li = lane & 31, lg = lane >> 5;
-  int pp, b, h, tile;
-  int64_t seg;
-  decode_unit(kKV ? a.sched_kv : a.sched_q, unit, (int)a.H, &a.nseg, pp, b, h, seg, tile);
-  const int w = a.w, r = a.r, L = a.L;
-  // Under a causal mask a key tile's work shrinks with its index: run low tiles first.
-  if (kKV && a.causal) tile = (L + kBwdRows - 1) / kBwdRows - 1 - tile;
+  const int w = a.w[p], r = a.r[p], L = a.L[p];
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const int64_t rstride = (int64_t)r * a.sn;
@@ -297,8 +274,10 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, u
   //   key units:   gradient MFMAs interleaved with the VALU, then S/dP of hh+1
   //                into the registers the VALU just consumed (their register
   //                budget has no room for a second S/dP set).
-  // Stages that do not run mark their outputs dead, so that the register
-  // allocator need not keep the stale values alive across the phase.
+  // S/dP of hh+1 is computed whether or not that half is active (on whatever
+  // the stage holds; the result is only consumed when it is), so that the
+  // registers are written on every path and never copied.  P/dS of a half
+  // that does not run is marked dead for the same reason.
 #define DLA_DEAD(x) x = __builtin_nondeterministic_value(x)
 #define DLA_BWD_PHASE(hh, blk, sg, ss, sv, S_cur, P_cur, S_nxt, P_nxt, pw_cur, sw_cur, pw_prv, sw_prv) \
   do {                                                                                           \
@@ -323,13 +302,9 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, u
           _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { DLA_DEAD(pw_cur[i_]); DLA_DEAD(sw_cur[i_]); } \
         }                                                                                        \
       }                                                                                          \
-      if (a_next) {                                                                              \
-        stage_sd(ss, 1 - (blk), S_nxt, P_nxt);                                                   \
-      } else {                                                                                   \
-        DLA_DEAD(S_nxt);                                                                         \
-        DLA_DEAD(P_nxt);                                                                         \
-      }                                                                                          \
+      stage_sd(ss, 1 - (blk), S_nxt, P_nxt);                                                     \
     }                                                                                            \
+    (void)a_next;                                                                                \
   } while (0)
 
   // Ring step j: phase 2j reads tiles j-1 and j; then wait until tile j+1
@@ -369,7 +344,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, u
   }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if (active(0)) stage_sd(&ring[0], 0, sx, px);
+  stage_sd(&ring[0], 0, sx, px);
 
   for (int j = 0; j < nt; ++j)
     ring_step(j, &ring[(j + 3) & 3], &ring[j & 3], &ring[(j + 1) & 3], &ring[(j + 3) & 3]);
@@ -379,37 +354,74 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, u
 #undef DLA_DEAD
   (void)kIns;
 
-  if (!wave_valid || own >= L) return;
-  const int64_t n = base_row + (int64_t)own * r;
-  const int st = cover_state(a, n, h);
-  const int64_t acc_off = ((int64_t)b * a.N + n) * a.H * kD + (int64_t)h * kD;
-  const int64_t out_off = head_off + n * a.sn;
+  // ---- epilogue: each wave's 32 owned rows go through LDS (chunk c of row i
+  // at c ^ (i & 15), 256 B per row and tensor), so that every global store
+  // covers 4 whole rows with 16 bytes per lane.  A row kept by this pattern
+  // alone gets its rounded gradient; a row that other patterns also keep gets
+  // this pattern's fp32 partial (sparse order), summed later by the finalize
+  // pass.
+  __syncthreads();                                     // the ring is free
+  constexpr int kTens = kKV ? 2 : 1;
+  char* wbase = (char*)ring + wave * (kTens * 8192);
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  auto put = [&](int t, const f32x16 (&acc)[2], float sc) __attribute__((always_inline)) {
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int eg = 0; eg < 4; ++eg) {
-      const int d0 = 32 * db + 8 * eg + 4 * lg;
-      const f32x16& x = acc0[db];
-      if (kKV) {
-        const f32x16& y = acc1[db];
-        emit4(st, a.dk_acc + acc_off, (__bf16*)a.dk + out_off, d0, a.scale * x[4 * eg],
-              a.scale * x[4 * eg + 1], a.scale * x[4 * eg + 2], a.scale * x[4 * eg + 3]);
-        emit4(st, a.dv_acc + acc_off, (__bf16*)a.dv + out_off, d0, y[4 * eg], y[4 * eg + 1],
-              y[4 * eg + 2], y[4 * eg + 3]);
-      } else {
-        emit4(st, a.dq_acc + acc_off, (__bf16*)a.dq + out_off, d0, a.scale * x[4 * eg],
-              a.scale * x[4 * eg + 1], a.scale * x[4 * eg + 2], a.scale * x[4 * eg + 3]);
+      for (int eg = 0; eg < 4; ++eg) {
+        const int ch = 8 * db + 2 * eg + lg;
+        const f32x4 v = {sc * acc[db][4 * eg], sc * acc[db][4 * eg + 1], sc * acc[db][4 * eg + 2],
+                         sc * acc[db][4 * eg + 3]};
+        *(lds_f32x4*)((lds_char*)wbase + t * 8192 + li * 256 + 16 * (ch ^ (li & 15))) = v;
+      }
+  };
+  if (wave_valid) {
+    put(0, acc0, a.scale);
+    if (kKV) put(1, acc1, 1.f);
+    const int cc = lane & 15;
+    const int64_t part_row0 = ((int64_t)b * a.H + h) * a.nsp[p] + seg * L + own0;
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const int rr = 4 * it + (lane >> 4);
+      const int ownr = own0 + rr;
+      if (ownr >= L) continue;
+      const int n = (int)base_row + ownr * r;
+      const bool shared = kept_count(a, n, h) > 1;
+      const int64_t out_off = head_off + (int64_t)n * a.sn + 4 * cc;
+      const int64_t part_off = (part_row0 + rr) * kD + 4 * cc;
+#pragma unroll
+      for (int t = 0; t < kTens; ++t) {
+        const f32x4 v = *(const lds_f32x4*)((const lds_char*)wbase + t * 8192 + rr * 256 + 16 * (cc ^ (rr & 15)));
+        const int g = kKV ? 1 + t : 0;               // 0: dQ, 1: dK, 2: dV
+        if (shared) {
+          *(f32x4*)(a.part[p][g] + part_off) = v;
+        } else {
+          __bf16* outp = (__bf16*)(g == 0 ? a.dq : g == 1 ? a.dk : a.dv) + out_off;
+          *(uint2*)outp = uint2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        }
       }
     }
+  }
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bwd_bf16_kernel(const AttnBwdArgs a) {
   __shared__ BwdStage ring[kBwdStages];
+  // Longest first: the schedules hand out the highest tile index first, which
+  // is the most work for a query tile; under a causal mask a key tile has the
+  // most work at index 0, so key tiles are taken in reverse.  Units that touch
+  // the same rows are spread over the launch (a burst of them would contend
+  // for the same L2 and memory channels).
   const uint32_t u = blockIdx.x;
-  if (u < (uint32_t)a.sched_kv.total) {
-    bwd_unit<true>(a, ring, u);
+  const bool kv = u < (uint32_t)a.sched_kv.total;
+  int p, b, h, tile;
+  int64_t seg;
+  decode_unit(kv ? a.sched_kv : a.sched_q, kv ? u : u - (uint32_t)a.sched_kv.total, (int)a.H, a.nseg,
+              p, b, h, seg, tile);
+  if (kv) {
+    if (a.causal) tile = (a.L[p] + kBwdRows - 1) / kBwdRows - 1 - tile;
+    bwd_unit<true>(a, ring, p, b, h, seg, tile);
   } else {
-    bwd_unit<false>(a, ring, u - (uint32_t)a.sched_kv.total);
+    bwd_unit<false>(a, ring, p, b, h, seg, tile);
   }
 }
 

@@ -82,4 +82,56 @@ hipError_t launch_bwd_prep(const BwdPrepArgs& a, int dtype, hipStream_t stream) 
   return hipGetLastError();
 }
 
+// Finalize: a row kept by several patterns gets the sum of their fp32 partial
+// gradients (each in its pattern's sparse order, where row n is entry n / r),
+// rounded once.  Rows kept by one pattern were written by the attention pass
+// and rows kept by none by the preprocessing pass.  A workgroup takes 32
+// consecutive rows of one (batch, head), eight lanes per row and eight d
+// values per lane.  Every load is issued unconditionally (a lane whose row a
+// pattern does not keep reads that pattern's first entry and discards it), so
+// a wave waits for memory once per tensor.  HBM bound.
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdFinalizeArgs a) {
+  const uint32_t b = blockIdx.x / a.nblk;
+  const uint32_t n = (blockIdx.x - b * a.nblk) * 32 + (threadIdx.x >> 3);
+  const int c = threadIdx.x & 7;
+  const uint32_t h = blockIdx.y;
+  if (n >= (uint32_t)a.N) return;
+  uint32_t kept = 0;
+  int cnt = 0;
+  uint32_t sp[kMaxP];
+  for (int p = 0; p < a.P; ++p) {
+    const uint32_t rp = (uint32_t)a.r[p];
+    const bool k = a.shift[p] >= 0 ? ((n ^ h) & (rp - 1)) == 0 : (n % rp) == (h % rp);
+    sp[p] = a.shift[p] >= 0 ? n >> a.shift[p] : n / rp;
+    kept |= (uint32_t)k << p;
+    cnt += k;
+  }
+  if (cnt < 2) return;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int64_t out_off = (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
+  for (int g = 0; g < 3; ++g) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < a.P; ++p) {
+      const bool k = (kept >> p) & 1;
+      const float* src = a.part[p][g] + (k ? (bh * a.nsp[p] + sp[p]) * kD + 8 * c : 0);
+      const float4 x = *(const float4*)src, y = *(const float4*)(src + 4);
+      if (k) {
+        acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
+        acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
+      }
+    }
+    *(uint4*)((__bf16*)a.grad[g] + out_off) =
+        uint4{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
+              pack_bf16(acc[6], acc[7])};
+  }
+}
+
+hipError_t launch_bwd_finalize(const BwdFinalizeArgs& a, hipStream_t stream) {
+  if (a.B * a.N * a.H == 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.B * a.nblk), (unsigned)a.H);
+  TimedLaunch tl("bwd_finalize", stream);
+  hipLaunchKernelGGL(bwd_finalize_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace dla

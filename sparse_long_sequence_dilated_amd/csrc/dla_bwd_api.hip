@@ -1,11 +1,11 @@
 // C ABI entry point of the backward pass (see include/dla.h).
 //
 // Launch sequence on the caller's stream: one preprocessing pass (D =
-// rowsum(dO*O), zero gradients for rows no pattern keeps), then one launch
-// per pattern.  Patterns other than the one keeping the most rows go first,
-// that one last; each launch's epilogue knows, per row, whether an earlier
-// or a later pattern keeps it, so fp32 accumulation only happens for rows
-// kept by several patterns and every gradient is rounded exactly once.
+// rowsum(dO*O) next to the combined LSE; zero gradients for rows no pattern
+// keeps), one attention pass over all patterns (rows kept by one pattern are
+// written directly; rows kept by several leave fp32 partials), and, with
+// several patterns, a finalize pass that sums the partials.  Every gradient
+// is rounded exactly once.
 #include <stdint.h>
 
 #include "dla_kernels.h"
@@ -38,7 +38,7 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
     return fail(DLA_E_UNSUPPORTED, "the backward pass is implemented for bf16 tensors");
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
-  float2* ld = (float2*)(wsb + pl.delta_off);
+  float2* ld = (float2*)(wsb + pl.ld_off);
 
   BwdPrepArgs pa{};
   pa.o = o;
@@ -60,20 +60,12 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
   hipError_t e = launch_bwd_prep(pa, pl.dtype, st);
   if (e != hipSuccess) return fail(DLA_E_HIP, "backward preprocessing launch: %s", hipGetErrorString(e));
 
-  int order[kMaxP], n = 0;
-  for (int i = 0; i < pl.P; ++i)
-    if (i != pl.prim) order[n++] = i;
-  order[n++] = pl.prim;
-
   AttnBwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
   a.dout = dout;
   a.ld = ld;
-  a.dq_acc = (float*)(wsb + pl.dq_off);
-  a.dk_acc = (float*)(wsb + pl.dk_off);
-  a.dv_acc = (float*)(wsb + pl.dv_off);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -88,28 +80,42 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
   a.scale_log2 = pl.scale * 1.4426950408889634f;
   a.P = pl.P;
   for (int i = 0; i < pl.P; ++i) {
-    a.r_all[i] = pl.r[i];
-    a.rank[order[i]] = i;
+    a.w[i] = pl.w[i];
+    a.r[i] = pl.r[i];
+    a.L[i] = pl.L[i];
+    a.nseg[i] = pl.nseg[i];
+    a.nsp[i] = pl.N / pl.r[i];
+    for (int g = 0; g < 3; ++g)
+      a.part[i][g] = pl.need_finalize ? (float*)(wsb + pl.part_g_off[i][g]) : nullptr;
   }
-  for (int i = 0; i < pl.P; ++i) {
-    const int p = order[i];
-    a.p = p;
-    a.w = pl.w[p];
-    a.r = pl.r[p];
-    a.L = pl.L[p];
-    a.nseg = pl.nseg[p];
-    Plan one = pl;  // one-pattern view for the unit schedule
-    one.P = 1;
-    one.w[0] = pl.w[p];
-    one.r[0] = pl.r[p];
-    one.L[0] = pl.L[p];
-    one.nseg[0] = pl.nseg[p];
-    make_schedule(one, 128, &a.sched_kv);
-    make_schedule(one, 128, &a.sched_q);
-    if (a.sched_kv.total + a.sched_q.total > 0x7FFFFFFF)
-      return fail(DLA_E_UNSUPPORTED, "too many work units for one launch");
-    e = launch_attn_bwd_bf16(a, st);
-    if (e != hipSuccess) return fail(DLA_E_HIP, "backward launch: %s", hipGetErrorString(e));
+  make_schedule(pl, 128, &a.sched_kv);
+  make_schedule(pl, 128, &a.sched_q);
+  if (a.sched_kv.total + a.sched_q.total > 0x7FFFFFFF)
+    return fail(DLA_E_UNSUPPORTED, "too many work units for one launch");
+  e = launch_attn_bwd_bf16(a, st);
+  if (e != hipSuccess) return fail(DLA_E_HIP, "backward launch: %s", hipGetErrorString(e));
+
+  if (pl.need_finalize) {
+    BwdFinalizeArgs f{};
+    for (int i = 0; i < pl.P; ++i) {
+      for (int g = 0; g < 3; ++g) f.part[i][g] = a.part[i][g];
+      f.r[i] = pl.r[i];
+      f.nsp[i] = pl.N / pl.r[i];
+      f.shift[i] = (pl.r[i] & (pl.r[i] - 1)) == 0 ? __builtin_ctz((unsigned)pl.r[i]) : -1;
+    }
+    f.grad[0] = dq;
+    f.grad[1] = dk;
+    f.grad[2] = dv;
+    f.sb = pl.sb;
+    f.sn = pl.sn;
+    f.sh = pl.sh;
+    f.B = pl.B;
+    f.N = pl.N;
+    f.H = pl.H;
+    f.P = pl.P;
+    f.nblk = (uint32_t)((pl.N + 31) / 32);
+    e = launch_bwd_finalize(f, st);
+    if (e != hipSuccess) return fail(DLA_E_HIP, "backward finalize launch: %s", hipGetErrorString(e));
   }
   return DLA_OK;
 }

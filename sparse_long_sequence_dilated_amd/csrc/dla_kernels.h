@@ -48,17 +48,15 @@ struct RowMapArgs {
   int H, w, r, L;
 };
 
-// Backward of one pattern: dK/dV units (one per key tile) and dQ units (one
-// per query tile) in one launch; both read the combined LSE and D.
+// Backward attention over all patterns in one launch: dK/dV units (one per
+// key tile) and dQ units (one per query tile), reading the combined LSE and D.
 struct AttnBwdArgs {
   const void* q;
   const void* k;
   const void* v;
   const void* dout;
   const float2* ld;        // (combined LSE * log2 e, D = rowsum(dO*O)) [B,H,N]
-  float* dq_acc;           // fp32 [B,N,H,D] accumulators (contiguous)
-  float* dk_acc;
-  float* dv_acc;
+  float* part[kMaxP][3];   // fp32 partial dQ, dK, dV of pattern p, [B,H,N/r,D] sparse order
   void* dq;                // outputs, input dtype, strides sb/sn/sh
   void* dk;
   void* dv;
@@ -66,13 +64,25 @@ struct AttnBwdArgs {
   int64_t B, N, H;
   int causal;
   float scale, scale_log2;
-  int p, w, r, L;          // the pattern of this launch
-  int64_t nseg;
   int P;
-  int r_all[kMaxP];        // dilation rate of every pattern
-  int rank[kMaxP];         // processing order of every pattern
-  Schedule sched_kv;       // dK/dV units (key tiles)
-  Schedule sched_q;        // dQ units (query tiles)
+  int w[kMaxP], r[kMaxP], L[kMaxP];
+  int64_t nseg[kMaxP];
+  int64_t nsp[kMaxP];      // N / r
+  Schedule sched_kv;       // dK/dV units (key tiles), all patterns
+  Schedule sched_q;        // dQ units (query tiles), all patterns
+};
+
+// Sum of the per-pattern partial gradients of rows kept by several patterns.
+struct BwdFinalizeArgs {
+  const float* part[kMaxP][3];
+  void* grad[3];           // dq, dk, dv (bf16, strides sb/sn/sh)
+  int64_t sb, sn, sh;
+  int64_t B, N, H;
+  int P;
+  int r[kMaxP];
+  int64_t nsp[kMaxP];
+  int shift[kMaxP];        // log2(r) when r is a power of two, else -1
+  uint32_t nblk;           // row blocks of 32 per (batch, head)
 };
 
 struct BwdPrepArgs {
@@ -112,5 +122,6 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_row_map(const RowMapArgs& a, hipStream_t stream);
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_prep(const BwdPrepArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_bwd_finalize(const BwdFinalizeArgs& a, hipStream_t stream);
 
 }  // namespace dla

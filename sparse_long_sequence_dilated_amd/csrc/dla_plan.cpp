@@ -102,14 +102,17 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan) {
 
   const size_t rows_all = (size_t)p.B * p.N * p.H;
   off = 0;
-  p.delta_off = off;
+  p.ld_off = off;
   off = align_up(off + rows_all * 2 * sizeof(float), 256);
-  p.dq_off = off;
-  off = align_up(off + rows_all * kD * sizeof(float), 256);
-  p.dk_off = off;
-  off = align_up(off + rows_all * kD * sizeof(float), 256);
-  p.dv_off = off;
-  off = align_up(off + rows_all * kD * sizeof(float), 256);
+  p.need_finalize = p.P > 1;
+  for (int i = 0; i < p.P; ++i)
+    for (int t = 0; t < 3; ++t) {
+      p.part_g_off[i][t] = (size_t)-1;
+      if (!p.need_finalize) continue;
+      const size_t rows = (size_t)p.B * p.H * (p.N / p.r[i]);
+      p.part_g_off[i][t] = off;
+      off = align_up(off + rows * kD * sizeof(float), 256);
+    }
   p.ws_bwd = off;
 
   // Useful (query, key) pairs; a count beyond int64 is refused.

@@ -45,9 +45,12 @@ struct Plan {
   size_t part_o_off[kMaxP];
   size_t part_lse_off[kMaxP];
   size_t ws_fwd;
-  // backward workspace: (LSE * log2 e, D = rowsum(dO*O)) [B,H,N] float pairs,
-  // fp32 accumulators [B,N,H,D]
-  size_t delta_off, dq_off, dk_off, dv_off;
+  // backward workspace: (LSE * log2 e, D = rowsum(dO*O)) [B,H,N] float pairs;
+  // with several patterns, per pattern the fp32 partial dQ, dK, dV [B,H,N/r,D]
+  // in sparse order (only rows that another pattern also keeps are written)
+  size_t ld_off;
+  size_t part_g_off[kMaxP][3];
+  bool need_finalize;           // some rows are kept by several patterns
   size_t ws_bwd;
   int64_t pairs;
 };
