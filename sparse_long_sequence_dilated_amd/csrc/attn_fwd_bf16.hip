@@ -10,12 +10,11 @@
 // kernel writes each pattern's normalised output and its per-row LSE.
 //
 // Data movement: K and V tiles of 64 sparse rows go from HBM straight into a
-// 4-stage LDS ring (64 KB) with global_load_lds_dwordx4, three tiles ahead of
-// use, so no registers stage them.  Each lane picks the source chunk that
-// belongs at its LDS slot, which yields swizzled layouts: K row-major with
-// chunk c of row i at c ^ t_swz(i) (conflict-free MFMA operand reads), V
-// row-major with chunk c of row i at c ^ 2*(i & 3) (conflict-free transposed
-// reads).  V^T operands come from ds_read_b64_tr_b16, which hands each lane
+// 4-stage LDS ring (64 KB) with buffer_load_dwordx4 ... lds, three tiles ahead
+// of use, so no registers stage them.  Each lane picks the source chunk that
+// belongs at its LDS slot, which yields one swizzled row-major layout for K
+// and V, chunk c of row i at c ^ u_swz(i), conflict-free both for the K
+// operand reads (ds_read_b128) and for the transposed V reads.  V^T operands come from ds_read_b64_tr_b16, which hands each lane
 // four consecutive keys of one head dimension.
 //
 // Compute: 4 waves x 64 query rows, two workgroups per CU.  A wave computes
@@ -45,12 +44,11 @@ struct __align__(16) FwdStage {
   uint4 v[kFwdBN * 8];  // 8 KB
 };
 
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
-
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs a) {
   __shared__ FwdStage ring[kStages];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int li = lane & 31, lg = lane >> 5;
 
   int p, b, h, tile;
@@ -65,12 +63,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
   const __bf16* Vh = (const __bf16*)a.v + head_off + base_row * a.sn;
 
   const int q0 = tile * kFwdBM;
-  const int qw0 = q0 + wave * 64;
+  const int qw0 = (q0 + wave * 64);  // wave-uniform (SGPR)
   const int kend = a.causal ? min(L, q0 + kFwdBM) : L;
   const int nkt = (kend + kFwdBN - 1) / kFwdBN;            // LDS tiles the workgroup stages
   const bool wave_active = qw0 < L;
   const int wave_kend = a.causal ? min(L, qw0 + 64) : L;
-  const int nh = wave_active ? (wave_kend + 31) / 32 : 0;   // half tiles this wave computes
+  const int nh = (wave_active ? (wave_kend + 31) / 32 : 0);  // half tiles this wave computes
   const float c = a.scale_log2;
 
   // Q as the B operand: lane (query li, group lg) holds d = 16*ks + 8*lg .. +8.
@@ -86,41 +84,49 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
 
   // ---- HBM -> LDS: wave w fills rows [16w, 16w+16) of a tile, 8 rows per instruction.
   // Lane l of instruction i lands at row 16w + 8i + l/8, slot l%8; it loads the
-  // logical chunk that belongs there.  Rows past the segment end load row L-1
-  // (finite values; the softmax masks those keys).
+  // logical chunk that belongs there.  The tile's first row is the buffer base
+  // (scalar), so a lane's byte offset is the same for every tile; rows past the
+  // segment end load row L-1 (finite values; the softmax masks those keys).
   const int dma_row0 = 16 * wave + (lane >> 3);
   const int dma_slot = lane & 7;
+  const uint32_t rsb = (uint32_t)(rstride * 2);       // bytes between sparse rows
+  const uint32_t span = 63u * rsb + 128u;              // bytes a tile's rows cover
+  // K and V share one swizzle (u_swz, a function of row % 16 = 8i + l/8), so
+  // a lane's source offset is the same for both.
+  uint32_t doff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    doff[i] = (uint32_t)(dma_row0 + 8 * i) * rsb + 16u * (uint32_t)(dma_slot ^ u_swz(8 * i + (lane >> 3)));
   auto issue_tile = [&](int kt, lds_u4* __restrict__ kdst, lds_u4* __restrict__ vdst) __attribute__((always_inline)) {
+    const int trow0 = kt * kFwdBN;
+    const int lim = L - 1 - trow0;                      // last valid row of the tile
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(Kh + (int64_t)trow0 * rstride, span);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(Vh + (int64_t)trow0 * rstride, span);
+    uint32_t o[2] = {doff[0], doff[1]};
+    if (lim < kFwdBN - 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        o[i] = (uint32_t)min(dma_row0 + 8 * i, lim) * rsb +
+               16u * (uint32_t)(dma_slot ^ u_swz(8 * i + (lane >> 3)));
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int row = dma_row0 + 8 * i;
-      const int grow = min(kt * kFwdBN + row, L - 1);
-      const __bf16* ks = Kh + (int64_t)grow * rstride + 8 * (dma_slot ^ t_swz(row));
-      const __bf16* vs = Vh + (int64_t)grow * rstride + 8 * (dma_slot ^ v_swz(row));
-      __builtin_amdgcn_global_load_lds((glb_void*)ks, (void __attribute__((address_space(3)))*)(kdst + 8 * (16 * wave + 8 * i)), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_void*)vs, (void __attribute__((address_space(3)))*)(vdst + 8 * (16 * wave + 8 * i)), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + 8 * (16 * wave + 8 * i)), 16, o[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + 8 * (16 * wave + 8 * i)), 16, o[i], 0, 0, 0);
     }
   };
 
   // ---- per-lane LDS operand addresses -----------------------------------------
-  // K operand (row 32kb + li, logical chunk 2ks + lg): byte offset within a stage's K.
-  int kaddr[2][4];
+  // K operand (row 32kb + li, logical chunk 2ks + lg): byte offset within a
+  // stage's K, + kb * 4096.
+  int kaddr[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int ks = 0; ks < 4; ++ks) kaddr[ks] = row_offset(lane, 0, ks);
+  // V^T operand via transposed reads (keys 16kk + 4*lg + {0..3, 8..11} of head
+  // dim 32db + li): byte offsets of the two 4-key halves, + kk * 2048.
+  int vlo[2], vhi[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kaddr[kb][ks] = 16 * r_index(32 * kb + li, 2 * ks + lg);
-  // V^T operand via transposed reads: lane l = 16m + t supplies row
-  // 16kk + 8*half + 4*(m/2) + t/4 and head dims 32db + 16(m%2) + 4(t%4) .. +4;
-  // it receives keys (16kk + 8*half + 4*lg) .. +3 of head dim 32db + li.
-  int vaddr[2];
-  {
-    const int t = lane & 15, m = lane >> 4;
-    const int rowoff = 4 * (m >> 1) + (t >> 2);
-    const int dchunk = 2 * (m & 1) + ((t & 3) >> 1);
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-      vaddr[db] = rowoff * 128 + (((4 * db + dchunk) ^ v_swz(rowoff)) << 4) + 8 * (t & 1);
-  }
+  for (int db = 0; db < 2; ++db) tr_offsets(lane, db, vlo[db], vhi[db]);
 
   f32x16 oacc[2][2];  // [db][qb]
 #pragma unroll
@@ -134,8 +140,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // ---- building blocks ------------------------------------------------------
   auto read_k = [&](const lds_u4* __restrict__ kst, int kb, bf16x8 (&kop)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kop[ks] = __builtin_bit_cast(bf16x8, *(const lds_u4*)((const lds_char*)kst + kaddr[kb][ks]));
+    for (int ks = 0; ks < 4; ++ks) kop[ks] = lds_read_b128(kst, kb * 4096 + kaddr[ks]);
   };
   auto read_v = [&](const lds_u4* __restrict__ vst, int half, bf16x8 (&vop)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -143,10 +148,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
 #pragma unroll
       for (int kl = 0; kl < 2; ++kl) {
         const int kk = 2 * half + kl;
-        const lds_char* base = (const lds_char*)vst + vaddr[db] + kk * 16 * 128;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + 8 * 128));
-        vop[db][kl] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        vop[db][kl] = lds_read_tr8(vst, vlo[db] + kk * 2048, vhi[db] + kk * 2048);
       }
   };
   auto mfma_s = [&](const bf16x8 (&kop)[4], f32x16 (&s)[2]) __attribute__((always_inline)) {
@@ -223,40 +225,78 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
       }
   };
 
-  f32x16 sa[2], sb[2];     // S of the current and the next half tile, [qb]
-  uint32_t p0[8], p1[8];   // packed P of query halves 0 and 1
+  // Four elements (e = 4g .. 4g+3) of P for block s with offset m: two packed
+  // bf16 words; the row-sum terms go to two accumulators (short dependency
+  // chains).
+  auto p_chunk = [&](const f32x16& s, float m, int g, uint32_t (&pw)[8], float& r0, float& r1) __attribute__((always_inline)) {
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g], c, -m));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 1], c, -m));
+    const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 2], c, -m));
+    const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 3], c, -m));
+    pw[2 * g] = pack_bf16(x0, x1);
+    pw[2 * g + 1] = pack_bf16(x2, x3);
+    r0 = dot2_bf16_ones(pw[2 * g], r0);
+    r1 = dot2_bf16_ones(pw[2 * g + 1], r1);
+  };
 
-  // One half-tile step: `cur` holds S_h, p0 holds P_h of query half 0.
+  f32x16 sa[2], sb[2];     // S of the current and the next half tile, [qb]
+  uint32_t pa[8], pb[8];   // packed P of query half 0, current and next (alternating)
+  uint32_t p1[8];          // packed P of query half 1
+
+  // One half-tile step, hand-interleaved: each group of two MFMAs is followed
+  // by the softmax VALU work of four elements that does not depend on them,
+  // and a scheduling fence keeps the compiler from regrouping (and from
+  // hoisting work, which would raise register pressure).
+  //   phase A: S_{h+1} = K_{h+1} Q^T (8 MFMAs) || P_h of query half 1
+  //   phase B: O^T += V_h^T P_h (8 MFMAs)      || P_{h+1} of query half 0
+  // `cur` holds S_h, p0c holds P_h of query half 0, p0n receives P_{h+1}.
   // kst_next: K of the stage holding half tile hh+1; vst: V of hh's stage.
-  auto step = [&](int hh, f32x16 (&cur)[2], f32x16 (&nxt)[2], const lds_u4* __restrict__ kst_next,
+  auto step = [&](int hh, f32x16 (&cur)[2], f32x16 (&nxt)[2], uint32_t (&p0c)[8],
+                  uint32_t (&p0n)[8], const lds_u4* __restrict__ kst_next,
                   const lds_u4* __restrict__ vst) __attribute__((always_inline)) {
     const bool has_next = hh + 1 < nh;
     bf16x8 vop[2][2], kop[4];
     if (has_next) {
       read_k(kst_next, (hh + 1) & 1, kop);
-      mfma_s(kop, nxt);                                   // phase A
-      const float rs1 = make_p(cur[1], m_run[1], p1);
-      DLA_INTERLEAVE(8, 6);
-      finish_p(cur[1], 1, rs1, p1);
+      read_v(vst, hh & 1, vop);
+      __builtin_amdgcn_sched_barrier(0);
+      float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {                   // phase A
+        nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[0][ks], ks ? nxt[0] : f32x16{}, 0, 0, 0);
+        nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[1][ks], ks ? nxt[1] : f32x16{}, 0, 0, 0);
+        p_chunk(cur[1], m_run[1], ks, p1, r0, r1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      finish_p(cur[1], 1, r0 + r1, p1);
       mask_s(hh + 1, nxt);
       apply_rescale();
-      read_v(vst, hh & 1, vop);
-      mfma_o(vop, p0, p1);                                // phase B
-      const float rs0 = make_p(nxt[0], m_run[0], p0);
-      DLA_INTERLEAVE(8, 6);
-      finish_p(nxt[0], 0, rs0, p0);
+      r0 = 0.f;
+      r1 = 0.f;
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {                   // phase B
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, uint4{p0c[4 * kl], p0c[4 * kl + 1], p0c[4 * kl + 2], p0c[4 * kl + 3]});
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, uint4{p1[4 * kl], p1[4 * kl + 1], p1[4 * kl + 2], p1[4 * kl + 3]});
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][kl], b0, oacc[db][0], 0, 0, 0);
+          oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][kl], b1, oacc[db][1], 0, 0, 0);
+          p_chunk(nxt[0], m_run[0], 2 * kl + db, p0n, r0, r1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      finish_p(nxt[0], 0, r0 + r1, p0n);
     } else {
       const float rs1 = make_p(cur[1], m_run[1], p1);
       finish_p(cur[1], 1, rs1, p1);
       apply_rescale();
       read_v(vst, hh & 1, vop);
-      mfma_o(vop, p0, p1);
+      mfma_o(vop, p0c, p1);
     }
   };
 
-  // One ring step j (j >= -3): issue tile j+3; at j == -1 start the pipeline
-  // (S_0 and P_0 of query half 0); at j >= 0 compute half tiles 2j and 2j+1,
-  // which read K of tiles j and j+1 and V of tile j.  Then wait until tile j+2
+  // One ring step j >= 0: issue tile j+3, compute half tiles 2j and 2j+1,
+  // which read K of tiles j and j+1 and V of tile j, then wait until tile j+2
   // is in LDS (tile j+3 may stay in flight) and synchronise.  Every DMA and
   // every LDS read of the loop lives in this one inlined body, and its
   // distinct restrict pointers tell the compiler that the DMA target never
@@ -266,16 +306,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
                        const lds_u4* __restrict__ k_j1) __attribute__((always_inline)) {
     const bool issue = j + 3 < nkt;
     if (issue) issue_tile(j + 3, dk, dv);
-    if (j == -1 && nh > 0) {
-      bf16x8 kop[4];
-      read_k(k_j1, 0, kop);
-      mfma_s(kop, sa);
-      mask_s(0, sa);
-      const float rs = make_p(sa[0], m_run[0], p0);
-      finish_p(sa[0], 0, rs, p0);
-    }
-    if (j >= 0 && 2 * j < nh) step(2 * j, sa, sb, k_j, v_j);
-    if (j >= 0 && 2 * j + 1 < nh) step(2 * j + 1, sb, sa, k_j1, v_j);
+    if (2 * j < nh) step(2 * j, sa, sb, pa, pb, k_j, v_j);
+    if (2 * j + 1 < nh) step(2 * j + 1, sb, sa, pb, pa, k_j1, v_j);
     if (issue) {
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     } else {
@@ -285,9 +317,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
     asm volatile("" ::: "memory");
   };
 
-  auto stage_k = [&](int j) __attribute__((always_inline)) { return (lds_u4*)ring[(j + kStages) % kStages].k; };
-  auto stage_v = [&](int j) __attribute__((always_inline)) { return (lds_u4*)ring[(j + kStages) % kStages].v; };
-  for (int j = -3; j < nkt; ++j)
+  // Prologue (kept out of the loop so that nothing in it is loop-invariant):
+  // tiles 0..2 in flight, S and P of half tile 0 once tile 0 has landed.
+  issue_tile(0, (lds_u4*)ring[0].k, (lds_u4*)ring[0].v);
+  if (nkt > 1) {
+    issue_tile(1, (lds_u4*)ring[1].k, (lds_u4*)ring[1].v);
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (nkt > 2) issue_tile(2, (lds_u4*)ring[2].k, (lds_u4*)ring[2].v);
+  if (nh > 0) {
+    bf16x8 kop[4];
+    read_k((const lds_u4*)ring[0].k, 0, kop);
+    mfma_s(kop, sa);
+    mask_s(0, sa);
+    const float rs = make_p(sa[0], m_run[0], pa);
+    finish_p(sa[0], 0, rs, pa);
+  }
+  if (nkt > 2) {
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  auto stage_k = [&](int j) __attribute__((always_inline)) { return (lds_u4*)ring[j % kStages].k; };
+  auto stage_v = [&](int j) __attribute__((always_inline)) { return (lds_u4*)ring[j % kStages].v; };
+  for (int j = 0; j < nkt; ++j)
     ring_step(j, stage_k(j + 3), stage_v(j + 3), stage_k(j), stage_v(j), stage_k(j + 1));
 
   if (!wave_active) return;
