@@ -66,8 +66,11 @@ __device__ __forceinline__ void divmod_r(uint32_t n, uint32_t r, int shift, uint
   }
 }
 
-// Block = 32 consecutive rows n of one (batch, head); 8 lanes per row.
-template <typename T>
+// Block = 32 consecutive rows n of one (batch, head); 8 lanes per row.  NP is
+// the number of patterns: fixed at compile time so that the per-pattern loops
+// unroll into straight-line code, and every load of a lane issues before the
+// first wait.
+template <typename T, int NP>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const uint32_t b = blockIdx.x / a.nblk;
   const uint32_t n = (blockIdx.x - b * a.nblk) * 32 + (threadIdx.x >> 3);
@@ -75,19 +78,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const uint32_t h = blockIdx.y;
   if (n >= (uint32_t)a.N) return;
 
-  uint32_t kept = 0, sidx[kMaxP];
+  uint32_t kept = 0, sidx[NP];
 #pragma unroll
-  for (int p = 0; p < kMaxP; ++p) {
-    sidx[p] = 0;
-    if (p < a.P) {
-      uint32_t q, m, qh, mh;
-      divmod_r(n, (uint32_t)a.r[p], a.shift[p], q, m);
-      divmod_r(h, (uint32_t)a.r[p], a.shift[p], qh, mh);
-      if (m == mh) {
-        kept |= 1u << p;
-        sidx[p] = q;  // sparse index of row n in pattern p
-      }
-    }
+  for (int p = 0; p < NP; ++p) {
+    uint32_t q, m, qh, mh;
+    divmod_r(n, (uint32_t)a.r[p], a.shift[p], q, m);
+    divmod_r(h, (uint32_t)a.r[p], a.shift[p], qh, mh);
+    kept |= (uint32_t)(m == mh) << p;
+    sidx[p] = q;  // sparse index of row n in pattern p (when it keeps the row)
   }
   const uint32_t prim_bit = 1u << a.prim;
   if (kept == prim_bit) return;  // only the pattern that wrote o keeps this row
@@ -103,36 +101,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
     if (c == 0) *lse_dst = -INFINITY;
     return;
   }
-  // Issue every load first (LSE and the 8-value slice of each kept pattern's
-  // output), so the memory latencies overlap; then merge.
-  float lv[kMaxP];
-  typename Vec8<T>::Raw raw[kMaxP];
+  // Every load first (LSE and the 8-value slice of each pattern's output), so
+  // the memory latencies overlap; then merge.  No branch surrounds a load: the
+  // pattern that wrote o/lse and the others differ only in the selected
+  // addresses, and a lane whose row pattern p does not keep reads entry 0 of
+  // that pattern's buffers and discards it.
+  float lv[NP];
+  typename Vec8<T>::Raw raw[NP];
 #pragma unroll
-  for (int p = 0; p < kMaxP; ++p) {
-    lv[p] = -INFINITY;
-    if (kept & (1u << p)) {
-      if (p == a.prim) {
-        lv[p] = *lse_dst;
-        raw[p] = Vec8<T>::load_raw(orow);
-      } else {
-        const int64_t m = bh * a.nsp[p] + sidx[p];
-        lv[p] = a.part_lse[p][m];
-        raw[p] = Vec8<T>::load_raw((const T*)a.part_o[p] + m * kD + 8 * c);
-      }
-    }
+  for (int p = 0; p < NP; ++p) {
+    const bool k = (kept >> p) & 1u;
+    const bool is_prim = p == a.prim;
+    const int64_t m = k ? bh * a.nsp[p] + sidx[p] : 0;
+    const T* src = is_prim ? (const T*)orow : (const T*)a.part_o[p] + m * kD + (k ? 8 * c : 0);
+    const float* lsrc = is_prim ? (const float*)lse_dst : a.part_lse[p] + m;
+    const float l = *lsrc;
+    raw[p] = Vec8<T>::load_raw(src);
+    lv[p] = k ? l : -INFINITY;
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int p = 0; p < kMaxP; ++p) mx = fmaxf(mx, lv[p]);
+  for (int p = 0; p < NP; ++p) mx = fmaxf(mx, lv[p]);
   float tot = 0.f;
 #pragma unroll
-  for (int p = 0; p < kMaxP; ++p)
-    if (kept & (1u << p)) tot += expf(lv[p] - mx);
+  for (int p = 0; p < NP; ++p) tot += (kept >> p) & 1u ? expf(lv[p] - mx) : 0.f;
   const float lse = mx + logf(tot);
 #pragma unroll
-  for (int p = 0; p < kMaxP; ++p) {
-    if (!(kept & (1u << p))) continue;
-    const float wt = expf(lv[p] - lse);
+  for (int p = 0; p < NP; ++p) {
+    const float wt = (kept >> p) & 1u ? expf(lv[p] - lse) : 0.f;
     float v[8];
     Vec8<T>::unpack(raw[p], v);
 #pragma unroll
@@ -142,14 +138,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   if (c == 0) *lse_dst = lse;
 }
 
+template <typename T>
+static void launch_combine_np(const CombineArgs& a, dim3 grid, hipStream_t stream) {
+  switch (a.P) {
+#define DLA_COMBINE_CASE(np) \
+    case np: hipLaunchKernelGGL((combine_kernel<T, np>), grid, dim3(256), 0, stream, a); break;
+    DLA_COMBINE_CASE(1) DLA_COMBINE_CASE(2) DLA_COMBINE_CASE(3) DLA_COMBINE_CASE(4)
+    DLA_COMBINE_CASE(5) DLA_COMBINE_CASE(6) DLA_COMBINE_CASE(7) DLA_COMBINE_CASE(8)
+    DLA_COMBINE_CASE(9) DLA_COMBINE_CASE(10) DLA_COMBINE_CASE(11) DLA_COMBINE_CASE(12)
+    DLA_COMBINE_CASE(13) DLA_COMBINE_CASE(14) DLA_COMBINE_CASE(15) DLA_COMBINE_CASE(16)
+#undef DLA_COMBINE_CASE
+    default: break;
+  }
+}
+
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream) {
   if (a.B * a.N * a.H == 0) return hipSuccess;
+  static_assert(kMaxP == 16, "one combine instantiation per pattern count");
   const dim3 grid((unsigned)(a.B * a.nblk), (unsigned)a.H);
   TimedLaunch tl("combine", stream);
   if (dtype == DLA_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, stream, a);
+    launch_combine_np<float>(a, grid, stream);
   else
-    hipLaunchKernelGGL(combine_kernel<__bf16>, grid, dim3(256), 0, stream, a);
+    launch_combine_np<__bf16>(a, grid, stream);
   return hipGetLastError();
 }
 
