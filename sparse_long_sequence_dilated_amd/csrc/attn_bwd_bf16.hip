@@ -264,6 +264,59 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     }
   };
 
+  // VALU chunk g (elements 4g .. 4g+3) of stage_valu with no mask.
+  auto valu_chunk = [&](const BwdStage* __restrict__ st, int blk, int g, const f32x16& S,
+                        const f32x16& P, uint32_t (&pw)[8], uint32_t (&sw)[8]) __attribute__((always_inline)) {
+    float l2[4], dd[4];
+    if (kKV) {
+      typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+      const lds_char* base = (const lds_char*)st->ld + 8 * (32 * blk + 8 * g + 4 * lg);
+      const f32x4 x0 = *(const lds_f32x4*)base;
+      const f32x4 x1 = *(const lds_f32x4*)(base + 16);
+      l2[0] = x0[0]; dd[0] = x0[1]; l2[1] = x0[2]; dd[1] = x0[3];
+      l2[2] = x1[0]; dd[2] = x1[1]; l2[3] = x1[2]; dd[3] = x1[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { l2[i] = lse2_own; dd[i] = d_own; }
+    }
+    float pv[4], dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * g + i;
+      pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, -l2[i]));
+      dv[i] = pv[i] * (P[e] - dd[i]);
+    }
+    if (kKV) {
+      pw[2 * g] = pack_bf16(pv[0], pv[1]);
+      pw[2 * g + 1] = pack_bf16(pv[2], pv[3]);
+    }
+    sw[2 * g] = pack_bf16(dv[0], dv[1]);
+    sw[2 * g + 1] = pack_bf16(dv[2], dv[3]);
+  };
+  // Steady state of a query unit: gradient products of half hh-1, S/dP of
+  // half hh+1 and dS of half hh, hand-interleaved in four groups separated by
+  // scheduling fences.  A group issues the LDS reads of its three MFMA
+  // operands, then four elements of VALU work (which covers the LDS latency),
+  // then the MFMAs, which run while the next group's VALU issues.  (Key units
+  // keep the compiler's schedule: their register budget has no room for it.)
+  auto fused_q = [&](const BwdStage* __restrict__ sg, int blk_g, const uint32_t (&swp)[8],
+                     const BwdStage* __restrict__ ss, int blk_s, f32x16& Sn, f32x16& Pn,
+                     int blk_v, const f32x16& S, const f32x16& P, uint32_t (&pw)[8], uint32_t (&sw)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int half = q >> 1, db = q & 1;
+      const int kko = (2 * blk_g + half) * 2048;
+      const bf16x8 ka = lds_read_tr8((const lds_u4*)sg->a, tlo[db] + kko, thi[db] + kko);
+      const bf16x8 xa = lds_read_b128((const lds_u4*)ss->a, blk_s * 4096 + roff[q]);
+      const bf16x8 xb = lds_read_b128((const lds_u4*)ss->b, blk_s * 4096 + roff[q]);
+      valu_chunk(ss, blk_v, q, S, P, pw, sw);
+      acc0[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, words_bf16(swp, half), acc0[db], 0, 0, 0);
+      Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, opa[q], q ? Sn : f32x16{}, 0, 0, 0);
+      Pn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, opb[q], q ? Pn : f32x16{}, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   f32x16 sx, px, sy, py;                       // S, dP of the even (x) / odd (y) half in flight
   uint32_t pwx[8], swx[8], pwy[8], swy[8];     // packed P, dS of the even / odd half
 
@@ -284,10 +337,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     const bool a_prev = active((hh) - 1), a_cur = active(hh), a_next = active((hh) + 1);        \
     const bool msk = need_mask(hh);                                                              \
     if (!kKV && a_prev && a_cur && a_next && !msk) {                                             \
-      stage_grad(sg, 1 - (blk), pw_prv, sw_prv);                                                 \
-      stage_sd(ss, 1 - (blk), S_nxt, P_nxt);                                                     \
-      stage_valu(hh, sv, blk, S_cur, P_cur, false, pw_cur, sw_cur);                              \
-      DLA_INTERLEAVE(12, 6);                                                                     \
+      fused_q(sg, 1 - (blk), sw_prv, ss, 1 - (blk), S_nxt, P_nxt, blk, S_cur, P_cur, pw_cur, sw_cur); \
     } else {                                                                                     \
       if (kKV && a_prev && a_cur && !msk) {                                                      \
         stage_grad(sg, 1 - (blk), pw_prv, sw_prv);                                               \
