@@ -138,8 +138,95 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   if (c == 0) *lse_dst = lse;
 }
 
+// Residue-class variant: the set of patterns that keep row n depends only on
+// n mod R (R = lcm of the rates) and on the head, so a workgroup that takes 32
+// rows n = rho + R*t of one class rho and one (batch, head) has one kept set
+// for all its lanes: rows only the primary pattern keeps are skipped by whole
+// workgroups, and each lane loads exactly the kept patterns' rows, with no
+// divergence and no discarded loads.  Grid: (row blocks, R, B*H).
+template <typename T, int NP>
+__global__ __launch_bounds__(256) void combine_class_kernel(const CombineArgs a) {
+  const uint32_t bhu = blockIdx.z;
+  const uint32_t h = bhu % (uint32_t)a.H, b = bhu / (uint32_t)a.H;
+  const uint32_t rho = blockIdx.y;
+  uint32_t kept = 0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    uint32_t q, m, qh, mh;
+    divmod_r(rho, (uint32_t)a.r[p], a.shift[p], q, m);
+    divmod_r(h, (uint32_t)a.r[p], a.shift[p], qh, mh);
+    kept |= (uint32_t)(m == mh) << p;
+  }
+  if (kept == (1u << a.prim)) return;  // only the pattern that wrote o keeps these rows
+  const uint32_t t = blockIdx.x * 32 + (threadIdx.x >> 3);
+  if (t >= a.rows_per_class) return;
+  const int c = threadIdx.x & 7;
+  const uint32_t n = rho + a.R * t;
+  const int64_t bh = (int64_t)b * a.H + h;
+  T* orow = (T*)a.o + (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
+  float* lse_dst = a.lse + bh * a.N + n;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (kept == 0) {  // no pattern keeps these rows
+    Vec8<T>::store(orow, acc);
+    if (c == 0) *lse_dst = -INFINITY;
+    return;
+  }
+  float lv[NP];
+  typename Vec8<T>::Raw raw[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    lv[p] = -INFINITY;
+    if (!((kept >> p) & 1u)) continue;                 // uniform
+    if (p == a.prim) {
+      lv[p] = *lse_dst;
+      raw[p] = Vec8<T>::load_raw(orow);
+    } else {
+      // sparse index n / r = rho / r + (R / r) * t
+      const uint32_t rp = (uint32_t)a.r[p];
+      const int64_t m = bh * a.nsp[p] + rho / rp + (a.R / rp) * t;
+      lv[p] = a.part_lse[p][m];
+      raw[p] = Vec8<T>::load_raw((const T*)a.part_o[p] + m * kD + 8 * c);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) mx = fmaxf(mx, lv[p]);
+  float tot = 0.f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    if ((kept >> p) & 1u) tot += expf(lv[p] - mx);
+  const float lse = mx + logf(tot);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (!((kept >> p) & 1u)) continue;
+    const float wt = expf(lv[p] - lse);
+    float v[8];
+    Vec8<T>::unpack(raw[p], v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wt, v[i], acc[i]);
+  }
+  Vec8<T>::store(orow, acc);
+  if (c == 0) *lse_dst = lse;
+}
+
 template <typename T>
 static void launch_combine_np(const CombineArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.R) {
+    const dim3 g((a.rows_per_class + 31) / 32, a.R, (unsigned)(a.B * a.H));
+    switch (a.P) {
+#define DLA_COMBINE_CASE(np) \
+      case np: hipLaunchKernelGGL((combine_class_kernel<T, np>), g, dim3(256), 0, stream, a); break;
+      DLA_COMBINE_CASE(1) DLA_COMBINE_CASE(2) DLA_COMBINE_CASE(3) DLA_COMBINE_CASE(4)
+      DLA_COMBINE_CASE(5) DLA_COMBINE_CASE(6) DLA_COMBINE_CASE(7) DLA_COMBINE_CASE(8)
+      DLA_COMBINE_CASE(9) DLA_COMBINE_CASE(10) DLA_COMBINE_CASE(11) DLA_COMBINE_CASE(12)
+      DLA_COMBINE_CASE(13) DLA_COMBINE_CASE(14) DLA_COMBINE_CASE(15) DLA_COMBINE_CASE(16)
+#undef DLA_COMBINE_CASE
+      default: break;
+    }
+    return;
+  }
   switch (a.P) {
 #define DLA_COMBINE_CASE(np) \
     case np: hipLaunchKernelGGL((combine_kernel<T, np>), grid, dim3(256), 0, stream, a); break;

@@ -102,6 +102,20 @@ extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const v
     if (nblk * pl.B > 0x7FFFFFFF)
       return fail(DLA_E_UNSUPPORTED, "B * N / 32 exceeds the launch grid");
     cb.nblk = (uint32_t)nblk;
+    // R = lcm of the rates divides N (every r divides its w, which divides N).
+    int64_t R = 1;
+    for (int i = 0; i < pl.P; ++i) {
+      int64_t g = R, x = pl.r[i];
+      while (x) { const int64_t t = g % x; g = x; x = t; }
+      R = R / g * pl.r[i];
+      if (R > pl.N) break;
+    }
+    const int64_t rpc = R <= pl.N ? pl.N / R : 0;
+    cb.R = 0;
+    if (rpc >= 32 && R <= 65535 && pl.B * pl.H <= 65535 && R * (int64_t)rpc == pl.N) {
+      cb.R = (uint32_t)R;
+      cb.rows_per_class = (uint32_t)rpc;
+    }
     e = launch_combine(cb, pl.dtype, st);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }

@@ -40,6 +40,10 @@ struct CombineArgs {
   int64_t nsp[kMaxP];      // N / r
   int shift[kMaxP];        // log2(r) when r is a power of two, else -1
   uint32_t nblk;           // row blocks of 32 per (batch, head)
+  // Residue-class launch (R > 0): rows n = rho + R*t with R = lcm of the
+  // rates share the set of patterns that keep them.
+  uint32_t R;              // 0: per-row launch
+  uint32_t rows_per_class; // N / R
 };
 
 struct RowMapArgs {

@@ -1,7 +1,8 @@
 """GPU forward parity against the CPU oracle (needs an MI355X).
 
 Small seeded cases span several tiles, ragged tails, uncovered rows, r > H,
-duplicate patterns, one-row segments and non-contiguous layouts; the
+duplicate patterns, one-row segments, non-contiguous layouts and both merge
+launch shapes (per residue class of n mod lcm(r), and per row); the
 workload configurations run at full size (full-tensor where the oracle is
 fast enough, sampled rows at 1M tokens).  Every call goes through the C ABI.
 """
@@ -34,6 +35,9 @@ SMALL = [
     (2, 512, 3, ((128, 1), (256, 2), (512, 4)), True, "f32", "bhnd"),
     (1, 256, 3, ((256, 4),), True, "f32", "bnhd"),                   # uncovered rows, fp32
     (1, 192, 2, ((3, 3), (192, 1)), False, "f32", "bnhd"),
+    # N / lcm(r) < 32: the merge runs per row instead of per residue class
+    (1, 256, 3, ((256, 1), (128, 16)), True, "bf16", "bnhd"),
+    (2, 512, 2, ((512, 1), (256, 32)), False, "f32", "bnhd"),
 ]
 
 
