@@ -126,11 +126,67 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdFinalizeArgs
   }
 }
 
+// Residue-class variant: rows n = rho + R*t (R = lcm of the rates) of one
+// (batch, head) are kept by one set of patterns, so a workgroup of 32 such
+// rows has a uniform kept set; classes kept by fewer than two patterns are
+// skipped by whole workgroups and each lane loads only the kept partials.
+// Grid: (row blocks, R, B*H).
+__global__ __launch_bounds__(256) void bwd_finalize_class_kernel(const BwdFinalizeArgs a) {
+  const uint32_t bhu = blockIdx.z;
+  const uint32_t h = bhu % (uint32_t)a.H, b = bhu / (uint32_t)a.H;
+  const uint32_t rho = blockIdx.y;
+  uint32_t kept = 0;
+  for (int p = 0; p < a.P; ++p) {
+    const uint32_t rp = (uint32_t)a.r[p];
+    const bool k = a.shift[p] >= 0 ? ((rho ^ h) & (rp - 1)) == 0 : (rho % rp) == (h % rp);
+    kept |= (uint32_t)k << p;
+  }
+  if (__builtin_popcount(kept) < 2) return;
+  const uint32_t t = blockIdx.x * 32 + (threadIdx.x >> 3);
+  if (t >= a.rows_per_class) return;
+  const int c = threadIdx.x & 7;
+  const uint32_t n = rho + a.R * t;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int64_t out_off = (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
+  float acc[3][8];
+#pragma unroll
+  for (int g = 0; g < 3; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+  for (int p = 0; p < a.P; ++p) {
+    if (!((kept >> p) & 1u)) continue;                 // uniform
+    const uint32_t rp = (uint32_t)a.r[p];
+    const int64_t row = bh * a.nsp[p] + rho / rp + (a.R / rp) * t;
+    float4 x[3], y[3];
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      const float* src = a.part[p][g] + row * kD + 8 * c;
+      x[g] = *(const float4*)src;
+      y[g] = *(const float4*)(src + 4);
+    }
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      acc[g][0] += x[g].x; acc[g][1] += x[g].y; acc[g][2] += x[g].z; acc[g][3] += x[g].w;
+      acc[g][4] += y[g].x; acc[g][5] += y[g].y; acc[g][6] += y[g].z; acc[g][7] += y[g].w;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 3; ++g)
+    *(uint4*)((__bf16*)a.grad[g] + out_off) =
+        uint4{pack_bf16(acc[g][0], acc[g][1]), pack_bf16(acc[g][2], acc[g][3]),
+              pack_bf16(acc[g][4], acc[g][5]), pack_bf16(acc[g][6], acc[g][7])};
+}
+
 hipError_t launch_bwd_finalize(const BwdFinalizeArgs& a, hipStream_t stream) {
   if (a.B * a.N * a.H == 0) return hipSuccess;
-  const dim3 grid((unsigned)(a.B * a.nblk), (unsigned)a.H);
   TimedLaunch tl("bwd_finalize", stream);
-  hipLaunchKernelGGL(bwd_finalize_kernel, grid, dim3(256), 0, stream, a);
+  if (a.R) {
+    const dim3 g((a.rows_per_class + 31) / 32, a.R, (unsigned)(a.B * a.H));
+    hipLaunchKernelGGL(bwd_finalize_class_kernel, g, dim3(256), 0, stream, a);
+  } else {
+    const dim3 grid((unsigned)(a.B * a.nblk), (unsigned)a.H);
+    hipLaunchKernelGGL(bwd_finalize_kernel, grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

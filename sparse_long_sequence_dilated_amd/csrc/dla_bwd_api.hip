@@ -114,6 +114,20 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
     f.H = pl.H;
     f.P = pl.P;
     f.nblk = (uint32_t)((pl.N + 31) / 32);
+    // R = lcm of the rates divides N (every r divides its w, which divides N).
+    int64_t R = 1;
+    for (int i = 0; i < pl.P; ++i) {
+      int64_t g = R, x = pl.r[i];
+      while (x) { const int64_t t = g % x; g = x; x = t; }
+      R = R / g * pl.r[i];
+      if (R > pl.N) break;
+    }
+    const int64_t rpc = R <= pl.N ? pl.N / R : 0;
+    f.R = 0;
+    if (rpc >= 32 && R <= 65535 && pl.B * pl.H <= 65535 && R * rpc == pl.N) {
+      f.R = (uint32_t)R;
+      f.rows_per_class = (uint32_t)rpc;
+    }
     e = launch_bwd_finalize(f, st);
     if (e != hipSuccess) return fail(DLA_E_HIP, "backward finalize launch: %s", hipGetErrorString(e));
   }

@@ -87,6 +87,8 @@ struct BwdFinalizeArgs {
   int64_t nsp[kMaxP];
   int shift[kMaxP];        // log2(r) when r is a power of two, else -1
   uint32_t nblk;           // row blocks of 32 per (batch, head)
+  uint32_t R;              // residue-class launch: R = lcm of the rates (0: per row)
+  uint32_t rows_per_class; // N / R
 };
 
 struct BwdPrepArgs {

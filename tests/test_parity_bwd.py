@@ -26,6 +26,9 @@ SMALL = [
     (1, 256, 3, ((4, 4), (64, 1)), True, "bnhd"),                    # one-row segments
     (2, 512, 3, ((128, 1), (512, 4)), True, "bhnd"),                 # [B,H,N,D] storage
     (1, 768, 2, ((768, 1), (768, 3)), False, "bnhd"),
+    # N / lcm(r) < 32: the finalize pass runs per row instead of per residue class
+    (1, 256, 3, ((256, 1), (128, 16)), True, "bnhd"),
+    (2, 512, 2, ((512, 1), (256, 32), (512, 2)), False, "bnhd"),
 ]
 
 
