@@ -20,7 +20,8 @@
 //
 // Compute: 8 waves x 32 query rows, two workgroups per CU (four waves per
 // SIMD, which is what hides the LDS, MFMA and exp latencies; a wave owns few
-// rows so that its registers fit that occupancy).  A wave computes
+// rows so that its registers fit that occupancy, and the launch bound holds
+// the compiler to the 128 VGPRs it allows).  A wave computes
 // S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on the rows, so a lane
 // holds one query's scores for 16 keys of a 32-key half tile) and
 // O^T += V^T P^T, feeding P^T to the MFMA straight from the S^T accumulator
@@ -48,11 +49,11 @@ struct __align__(16) FwdStage {
   uint4 v[kFwdBN * 8];  // 8 KB
 };
 
-__global__ __launch_bounds__(512, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs a) {
+__global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs a) {
   __shared__ FwdStage ring[kStages];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, lg = lane >> 5;
 
   int p, b, h, tile;
@@ -88,19 +89,26 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // instruction per tensor; lane l lands at row 8w + l/8, slot l%8, and loads
   // the logical chunk that belongs there (u_swz depends on row % 16).  The
   // tile's first row is the buffer base (scalar), so a lane's byte offset is
-  // the same for every tile; rows past the segment end load row L-1 (finite
-  // values; the softmax masks those keys).
+  // the same for every tile; rows past the segment end (only in the tile
+  // holding row L-1) load row L-1 (finite values; the softmax masks those
+  // keys).  Tiles are issued in order, so the tile base advances by a
+  // constant instead of being recomputed.
   const int dma_row = 8 * wave + (lane >> 3);
   const uint32_t rsb = (uint32_t)(rstride * 2);       // bytes between sparse rows
   const uint32_t span = 63u * rsb + 128u;              // bytes a tile's rows cover
   const uint32_t dchunk = 16u * (uint32_t)((lane & 7) ^ u_swz(dma_row));
   const uint32_t doff = (uint32_t)dma_row * rsb + dchunk;
+  const int tail_kt = (L - 1) / kFwdBN;
+  const uint32_t otail = (uint32_t)min(dma_row, L - 1 - tail_kt * kFwdBN) * rsb + dchunk;
+  const int64_t tile_bytes = (int64_t)kFwdBN * rstride * 2;
+  const char* kcur = (const char*)Kh;
+  const char* vcur = (const char*)Vh;
   auto issue_tile = [&](int kt, FwdStage* __restrict__ dst) __attribute__((always_inline)) {
-    const int trow0 = kt * kFwdBN;
-    const int lim = L - 1 - trow0;                      // last valid row of the tile
-    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(Kh + (int64_t)trow0 * rstride, span);
-    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(Vh + (int64_t)trow0 * rstride, span);
-    const uint32_t o = lim < kFwdBN - 1 ? (uint32_t)min(dma_row, lim) * rsb + dchunk : doff;
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kcur, span);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vcur, span);
+    kcur += tile_bytes;
+    vcur += tile_bytes;
+    const uint32_t o = kt == tail_kt ? otail : doff;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst->k + 8 * (8 * wave)), 16, o, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst->v + 8 * (8 * wave)), 16, o, 0, 0, 0);
   };
@@ -119,13 +127,18 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
   float pend = 1.f;                       // O rescale factor owed before O's next update
 
   // ---- building blocks --------------------------------------------------------
-  // S_h = K_h Q^T of half tile h (block blk of its stage).
-  auto mfma_s = [&](const FwdStage* __restrict__ st, int blk, f32x16& s) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 kop = lds_read_b128((const lds_u4*)st->k, blk * 4096 + kaddr[ks]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], ks ? s : f32x16{}, 0, 0, 0);
-    }
+  // K operand of step ks of S_h = K_h Q^T (half tile h in block blk of its stage).
+  auto read_k = [&](const FwdStage* __restrict__ st, int blk, int ks) __attribute__((always_inline)) {
+    return lds_read_b128((const lds_u4*)st->k, blk * 4096 + kaddr[ks]);
+  };
+  // S_h from its four K operands, the first two read ahead by the caller.
+  auto mfma_s = [&](const FwdStage* __restrict__ st, int blk, const bf16x8& k0, const bf16x8& k1, f32x16& s) __attribute__((always_inline)) {
+    const bf16x8 k2 = read_k(st, blk, 2);
+    const bf16x8 k3 = read_k(st, blk, 3);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qop[0], f32x16{}, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qop[1], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2, qop[2], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k3, qop[3], s, 0, 0, 0);
   };
   // Four elements (e = 4g .. 4g+3) of P with offset m: two packed bf16 words;
   // the row-sum terms go to two accumulators.
@@ -139,13 +152,19 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
     r0 = dot2_bf16_ones(pw[2 * g], r0);
     r1 = dot2_bf16_ones(pw[2 * g + 1], r1);
   };
-  // One O^T MFMA: head-dim block db, 16-key step kl of the half tile in block
-  // blk of stage st, with the packed P words of that half.
-  auto mfma_o1 = [&](const FwdStage* __restrict__ st, int blk, int db, int kl, const uint32_t (&pw)[8]) __attribute__((always_inline)) {
+  // V^T operand of one O^T MFMA: head-dim block db, 16-key step kl of the
+  // half tile in block blk of stage st.
+  auto read_v = [&](const FwdStage* __restrict__ st, int blk, int db, int kl) __attribute__((always_inline)) {
     const int kk = 2 * blk + kl;
-    const bf16x8 vop = lds_read_tr8((const lds_u4*)st->v, vlo[db] + kk * 2048, vhi[db] + kk * 2048);
+    return lds_read_tr8((const lds_u4*)st->v, vlo[db] + kk * 2048, vhi[db] + kk * 2048);
+  };
+  // One O^T MFMA with the packed P words of that half tile.
+  auto mfma_o = [&](const bf16x8& vop, int db, int kl, const uint32_t (&pw)[8]) __attribute__((always_inline)) {
     const bf16x8 pb = __builtin_bit_cast(bf16x8, uint4{pw[4 * kl], pw[4 * kl + 1], pw[4 * kl + 2], pw[4 * kl + 3]});
     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, oacc[db], 0, 0, 0);
+  };
+  auto mfma_o1 = [&](const FwdStage* __restrict__ st, int blk, int db, int kl, const uint32_t (&pw)[8]) __attribute__((always_inline)) {
+    mfma_o(read_v(st, blk, db, kl), db, kl, pw);
   };
   // Accept P computed with the running offset, or redo it with the true maximum.
   auto finish_p = [&](const f32x16& s, float rs, uint32_t (&pw)[8]) __attribute__((always_inline)) {
@@ -197,25 +216,39 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // 1-blk) interleaved with P_hh (block blk), then S_{hh+1} from stage ss.
   // Hand-interleaved: each O MFMA is followed by four elements of VALU work
   // that do not depend on it, with scheduling fences between the groups.
+  // Every LDS operand is read one group ahead of its MFMA: the V^T operand
+  // of group g+1 and, in the last group, the first two K operands of
+  // S_{hh+1} (both tiles are in LDS for the whole phase).
   auto phase = [&](int hh, int blk, const FwdStage* __restrict__ so, const FwdStage* __restrict__ ss,
                    uint32_t (&pprev)[8], uint32_t (&pcur)[8]) __attribute__((always_inline)) {
     mask_s(hh, s);
     float r0 = 0.f, r1 = 0.f;
+    bf16x8 k0, k1;
     if (hh > 0) {
       apply_rescale();
+      bf16x8 vn = read_v(so, 1 - blk, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        mfma_o1(so, 1 - blk, g & 1, g >> 1, pprev);
+        const bf16x8 vc = vn;
+        if (g < 3) {
+          vn = read_v(so, 1 - blk, (g + 1) & 1, (g + 1) >> 1);
+        } else {
+          k0 = read_k(ss, 1 - blk, 0);
+          k1 = read_k(ss, 1 - blk, 1);
+        }
+        mfma_o(vc, g & 1, g >> 1, pprev);
         p_chunk(s, m_run, g, pcur, r0, r1);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      k0 = read_k(ss, 1 - blk, 0);
+      k1 = read_k(ss, 1 - blk, 1);
 #pragma unroll
       for (int g = 0; g < 4; ++g) p_chunk(s, m_run, g, pcur, r0, r1);
     }
     finish_p(s, r0 + r1, pcur);
-    if (hh + 1 < nh) mfma_s(ss, 1 - blk, s);
+    if (hh + 1 < nh) mfma_s(ss, 1 - blk, k0, k1, s);
   };
 
   // Ring step j: phase 2j reads V of tile j-1 and K/V of tile j; then wait
@@ -251,7 +284,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_kernel(const AttnFwdArgs
   }
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if (nh > 0) mfma_s(&ring[0], 0, s);
+  if (nh > 0) mfma_s(&ring[0], 0, read_k(&ring[0], 0, 0), read_k(&ring[0], 0, 1), s);
 
   for (int j = 0; j < nkt; ++j)
     ring_step(j, &ring[(j + 3) & 3], &ring[j & 3], &ring[(j + 1) & 3], &ring[(j + 3) & 3]);
