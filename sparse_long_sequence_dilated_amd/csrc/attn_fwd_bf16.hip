@@ -10,8 +10,10 @@
 // kernel writes each pattern's normalised output and its per-row LSE.
 //
 // Data movement: K and V tiles of 64 sparse rows go from HBM straight into a
-// 4-stage LDS ring (64 KB) with buffer_load_dwordx4 ... lds, two steps ahead
-// of use, so no registers stage them.  Each lane picks the source chunk that
+// 5-stage LDS ring (80 KB, so two workgroups fill the CU's 160 KB) with
+// buffer_load_dwordx4 ... lds, so no registers stage them.  The workgroup
+// synchronises once per two tiles: each barrier both publishes the two tiles
+// loaded one window earlier and frees the two stages the next loads reuse.  Each lane picks the source chunk that
 // belongs at its LDS slot, which yields one swizzled row-major layout for K
 // and V, chunk c of row i at c ^ u_swz(i), conflict-free both for the K
 // operand reads (ds_read_b128) and for the transposed V reads
@@ -40,9 +42,13 @@ namespace dla {
 
 constexpr int kFwdBM = 256;      // sparse query rows per workgroup (8 waves x 32)
 constexpr int kFwdBN = 64;       // keys per LDS tile (two 32-key half tiles)
-constexpr int kStages = 4;       // LDS ring depth
+constexpr int kStages = 5;       // LDS ring depth
 constexpr int kFwdWaves = 8;
 constexpr float kSumLimit = 65536.f;
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8).  Issued through the builtin, not inline asm, so that the compiler's
+// own wait insertion sees them and knows which loads have completed.
+constexpr int kVmcnt0 = 0x0F70;
 
 struct __align__(16) FwdStage {
   uint4 k[kFwdBN * 8];  // 8 KB
@@ -251,50 +257,59 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
     if (hh + 1 < nh) mfma_s(ss, 1 - blk, k0, k1, s);
   };
 
-  // Ring step j: phase 2j reads V of tile j-1 and K/V of tile j; then wait
-  // until tile j+1 is in LDS (tile j+2 may stay in flight), synchronise,
-  // refill the stage of tile j-1 with tile j+3, and run phase 2j+1 on tiles j
-  // and j+1.  The distinct restrict pointers tell the compiler that the DMA
-  // target is not read after the refill, so it adds no waits of its own.
-  auto ring_step = [&](int j, const FwdStage* __restrict__ sp, const FwdStage* __restrict__ sc,
-                       const FwdStage* __restrict__ sn, FwdStage* __restrict__ si) __attribute__((always_inline)) {
-    if (2 * j < nh) phase(2 * j, 0, sp, sc, pb, pa);
-    if (j + 2 < nkt) {
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Window after barrier B_j (j even): phases 2j+1 .. 2j+4 read tiles j,
+  // j+1 and j+2 (V of halves 2j .. 2j+3, K of halves 2j+2 .. 2j+5).  At B_j
+  // every wave has finished phase 2j, so the stages of tiles j-2 and j-1 are
+  // free and take tiles j+3 and j+4, which the next window's barrier waits
+  // for.  Tile t lives in stage t % 5; the distinct restrict pointers tell
+  // the compiler that the DMA targets are not read in the window, so it adds
+  // no waits of its own.
+  auto window = [&](int j, const FwdStage* __restrict__ s0, const FwdStage* __restrict__ s1,
+                    const FwdStage* __restrict__ s2, FwdStage* __restrict__ i3,
+                    FwdStage* __restrict__ i4) __attribute__((always_inline)) {
+    if (j > 0) {
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (j + 3 < nkt) issue_tile(j + 3, si);
-    if (2 * j + 1 < nh) phase(2 * j + 1, 1, sc, sn, pa, pb);
+    if (j + 3 < nkt) issue_tile(j + 3, i3);
+    if (j + 4 < nkt) issue_tile(j + 4, i4);
+    if (2 * j + 1 < nh) phase(2 * j + 1, 1, s0, s1, pa, pb);
+    if (2 * j + 2 < nh) phase(2 * j + 2, 0, s0, s1, pb, pa);
+    if (2 * j + 3 < nh) phase(2 * j + 3, 1, s1, s2, pa, pb);
+    if (2 * j + 4 < nh) phase(2 * j + 4, 0, s1, s2, pb, pa);
   };
 
-  // Prologue (out of the loop): tiles 0..2 in flight, S of half tile 0 once
-  // tile 0 has landed.
+  // Prologue: tiles 0..2 in LDS (the first window reads all three; stages 3
+  // and 4 are still unused, so B_0 needs no barrier), S and P of half tile 0.
   issue_tile(0, &ring[0]);
   if (nkt > 1) issue_tile(1, &ring[1]);
   if (nkt > 2) issue_tile(2, &ring[2]);
-  if (nkt > 2) {
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  } else if (nkt > 1) {
-    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if (nh > 0) mfma_s(&ring[0], 0, read_k(&ring[0], 0, 0), read_k(&ring[0], 0, 1), s);
-
-  for (int j = 0; j < nkt; ++j)
-    ring_step(j, &ring[(j + 3) & 3], &ring[j & 3], &ring[(j + 1) & 3], &ring[(j + 3) & 3]);
+  if (nh > 0) {
+    mfma_s(&ring[0], 0, read_k(&ring[0], 0, 0), read_k(&ring[0], 0, 1), s);
+    phase(0, 0, &ring[0], &ring[0], pb, pa);
+  }
+  for (int j = 0, t0 = 0; j < nkt; j += 2) {
+    // t0 = j % 5
+    const int t1 = t0 == 4 ? 0 : t0 + 1, t2 = t1 == 4 ? 0 : t1 + 1;
+    const int t3 = t2 == 4 ? 0 : t2 + 1, t4 = t3 == 4 ? 0 : t3 + 1;
+    window(j, &ring[t0], &ring[t1], &ring[t2], &ring[t3], &ring[t4]);
+    t0 = t2;
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      asm volatile("" ::: "memory");
 
   if (!wave_active) return;
   // Drain: O update with the wave's last P (half nh-1, in tile (nh-1)/2).
   apply_rescale();
   {
     const int hl = nh - 1;
-    const FwdStage* st = &ring[(hl >> 1) & 3];
+    const FwdStage* st = &ring[(hl >> 1) % kStages];
     if (hl & 1) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) mfma_o1(st, 1, g & 1, g >> 1, pb);
