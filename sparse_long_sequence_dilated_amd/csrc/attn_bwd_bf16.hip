@@ -36,6 +36,7 @@
 namespace dla {
 
 constexpr int kBwdRows = 128;   // rows a unit owns (4 waves x 32)
+static_assert(kBwdRows == kBwdUnitRows, "the schedules and the kernel must agree on the unit size");
 constexpr int kBwdTile = 64;    // streamed rows per LDS tile
 constexpr int kBwdStages = 4;   // LDS ring depth (tiles in flight: 2)
 

@@ -88,8 +88,8 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
     for (int g = 0; g < 3; ++g)
       a.part[i][g] = pl.need_finalize ? (float*)(wsb + pl.part_g_off[i][g]) : nullptr;
   }
-  make_schedule(pl, 128, &a.sched_kv);
-  make_schedule(pl, 128, &a.sched_q);
+  make_schedule(pl, kBwdUnitRows, &a.sched_kv);
+  make_schedule(pl, kBwdUnitRows, &a.sched_q);
   if (a.sched_kv.total + a.sched_q.total > 0x7FFFFFFF)
     return fail(DLA_E_UNSUPPORTED, "too many work units for one launch");
   e = launch_attn_bwd_bf16(a, st);

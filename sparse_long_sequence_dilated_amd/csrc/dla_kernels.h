@@ -126,6 +126,8 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_row_map(const RowMapArgs& a, hipStream_t stream);
+// Rows a backward work unit owns (the tile size of both schedules).
+constexpr int kBwdUnitRows = 128;
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_prep(const BwdPrepArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_bwd_finalize(const BwdFinalizeArgs& a, hipStream_t stream);
