@@ -136,11 +136,83 @@ int dla_row_map(const dla_desc* desc, int64_t N, int32_t H, int32_t pattern, int
 int dla_pair_count(const dla_desc* desc, const dla_shape* shape, int64_t* pairs);
 
 /*
+ * ---- Sequence shards ([G] 方法论, the distributed item) ----
+ *
+ * The pages scale past one device by cutting the sequence along its length:
+ * each device holds one contiguous piece, a segment that fits in a piece is
+ * handled locally, and for a segment that crosses devices the devices
+ * exchange its sparsified keys and values, so that each one attends its own
+ * queries to the whole segment; the cost of the exchange does not grow with
+ * the sequence.  These entry points are one device's share of that scheme:
+ * the collective itself (an all-gather over the devices of a segment) is the
+ * caller's.
+ *
+ * The device holds rows [shard_start, shard_start + N) of a sequence of
+ * total_rows rows, where N is shape->N, shard_start is a multiple of N and N
+ * divides total_rows.  Every w divides total_rows.  A pattern with w <= N
+ * must divide N (its segments are local).  A pattern with w > N "spans":
+ * N must divide w, r must divide N and N / r must be a multiple of 64.
+ * Shards are implemented for bf16.
+ */
+typedef struct {
+  int64_t total_rows;
+  int64_t shard_start;
+} dla_shard;
+
+/*
+ * Validate a descriptor, a shard shape and its place in the sequence on the
+ * host and report the workspace bytes dla_forward_shard needs (the out
+ * pointer may be NULL).  Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
+ */
+int dla_plan_check_shard(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
+                         size_t* ws_fwd_bytes);
+
+/*
+ * Number of (query, key) pairs the shard evaluates: the pairs of
+ * dla_pair_count whose query row lies in the shard.  Host only.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
+ */
+int dla_pair_count_shard(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
+                         int64_t* pairs);
+
+/*
+ * This device's part of the exchange for spanning pattern `pattern`: its
+ * sparse rows of the segment that contains the shard,
+ *   out[b][h][i][:] = x[b][(h mod r) + i * r][h][:],  i < N / r,
+ * written as a contiguous bf16 [B, H, N/r, D] tensor (x is k or v of the
+ * shard, strides of `shape`).  Gathering these parts from the w/N devices of
+ * the segment in device order gives the [w/N, B, H, N/r, D] buffer that
+ * dla_forward_shard reads.  out is a device pointer the caller owns.
+ * Errors: DLA_E_INVALID (null/misaligned pointer, pattern index out of range
+ * or a pattern that does not span), DLA_E_UNSUPPORTED, DLA_E_HIP.
+ */
+int dla_shard_gather(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
+                     int32_t pattern, const void* x, void* out, void* stream);
+
+/*
+ * Forward pass of one shard: writes o and lse for the shard's rows (q, k, v,
+ * o, lse shaped by `shape`, i.e. N = the shard length), equal to the rows
+ * [shard_start, shard_start + N) that dla_forward computes on the whole
+ * sequence.  Local patterns read the shard's k and v.  For every spanning
+ * pattern p, ext_k[p] and ext_v[p] are device pointers to the gathered parts
+ * of the segment that contains the shard, [w_p/N, B, H, N/r_p, D] bf16 as
+ * dla_shard_gather lays them out; entries of other patterns are ignored
+ * (the arrays are host memory with num_patterns entries, or NULL when no
+ * pattern spans).  ws must hold dla_plan_check_shard's size.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_WORKSPACE, DLA_E_HIP.
+ */
+int dla_forward_shard(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
+                      const void* q, const void* k, const void* v, const void* const* ext_k,
+                      const void* const* ext_v, void* o, float* lse, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
  * Opt-in launch timing, a profiling aid.  While enabled (on != 0), every
  * kernel launch made by dla_forward / dla_backward is bracketed by two HIP
  * events recorded on the caller's stream (host-side bookkeeping only; the
  * kernels are unchanged).  Kernel families: "attn_fwd" (bf16 forward
- * attention), "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd".
+ * attention), "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd",
+ * "bwd_finalize", "shard_gather".
  */
 int dla_timing_enable(int on);
 

@@ -65,20 +65,29 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   int p, b, h, tile;
   int64_t seg;
   decode_unit(a.sched, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile);
-  const int w = a.w[p], r = a.r[p], L = a.L[p];
+  // L query rows (local), Lk key rows; local query row i is row qoff + i of
+  // the segment (qoff = 0 and Lk = L except for a segment that spans
+  // several sequence shards, whose keys come from the gathered buffers).
+  const int w = a.w[p], r = a.r[p], L = a.L[p], Lk = a.Lk[p], qoff = a.qoff[p];
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const int64_t rstride = (int64_t)r * a.sn;  // elements between consecutive sparse rows
   const __bf16* Qh = (const __bf16*)a.q + head_off + base_row * a.sn;
-  const __bf16* Kh = (const __bf16*)a.k + head_off + base_row * a.sn;
-  const __bf16* Vh = (const __bf16*)a.v + head_off + base_row * a.sn;
+  const bool ext = a.ext_k[p] != nullptr;
+  const int64_t cr = a.nsp[p];                 // rows per gathered chunk
+  const __bf16* Kh = ext ? (const __bf16*)a.ext_k[p] + ((int64_t)b * a.H + h) * cr * kD
+                         : (const __bf16*)a.k + head_off + base_row * a.sn;
+  const __bf16* Vh = ext ? (const __bf16*)a.ext_v[p] + ((int64_t)b * a.H + h) * cr * kD
+                         : (const __bf16*)a.v + head_off + base_row * a.sn;
+  const int64_t kstride = ext ? (int64_t)kD : rstride;   // elements between key rows
 
   const int q0 = tile * kFwdBM;
   const int qw0 = q0 + wave * 32;                          // this wave's first query row
-  const int kend = a.causal ? min(L, q0 + kFwdBM) : L;
+  const int qg0 = qoff + q0, qgw0 = qoff + qw0;            // the same as rows of the segment
+  const int kend = a.causal ? min(Lk, qg0 + kFwdBM) : Lk;
   const int nkt = (kend + kFwdBN - 1) / kFwdBN;            // LDS tiles the workgroup stages
   const bool wave_active = qw0 < L;
-  const int wave_kend = a.causal ? min(L, qw0 + 32) : L;
+  const int wave_kend = a.causal ? min(Lk, qgw0 + 32) : Lk;
   const int nh = wave_active ? (wave_kend + 31) / 32 : 0;  // half tiles this wave computes
   const float c = a.scale_log2;
 
@@ -100,13 +109,18 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // keys).  Tiles are issued in order, so the tile base advances by a
   // constant instead of being recomputed.
   const int dma_row = 8 * wave + (lane >> 3);
-  const uint32_t rsb = (uint32_t)(rstride * 2);       // bytes between sparse rows
+  const uint32_t rsb = (uint32_t)(kstride * 2);       // bytes between key rows
   const uint32_t span = 63u * rsb + 128u;              // bytes a tile's rows cover
   const uint32_t dchunk = 16u * (uint32_t)((lane & 7) ^ u_swz(dma_row));
   const uint32_t doff = (uint32_t)dma_row * rsb + dchunk;
-  const int tail_kt = (L - 1) / kFwdBN;
-  const uint32_t otail = (uint32_t)min(dma_row, L - 1 - tail_kt * kFwdBN) * rsb + dchunk;
-  const int64_t tile_bytes = (int64_t)kFwdBN * rstride * 2;
+  const int tail_kt = (Lk - 1) / kFwdBN;
+  const uint32_t otail = (uint32_t)min(dma_row, Lk - 1 - tail_kt * kFwdBN) * rsb + dchunk;
+  const int64_t tile_bytes = (int64_t)kFwdBN * kstride * 2;
+  // Gathered keys: after cr / 64 tiles the next chunk (next device) of this
+  // (batch, head) starts B*H chunks further on.
+  const int tiles_per_chunk = ext ? (int)(cr / kFwdBN) : 0x7FFFFFFF;
+  const int64_t chunk_jump = ext ? ((int64_t)a.B * a.H - 1) * cr * kD * 2 : 0;
+  int tc = 0;
   const char* kcur = (const char*)Kh;
   const char* vcur = (const char*)Vh;
   auto issue_tile = [&](int kt, FwdStage* __restrict__ dst) __attribute__((always_inline)) {
@@ -114,6 +128,11 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vcur, span);
     kcur += tile_bytes;
     vcur += tile_bytes;
+    if (++tc == tiles_per_chunk) {
+      tc = 0;
+      kcur += chunk_jump;
+      vcur += chunk_jump;
+    }
     const uint32_t o = kt == tail_kt ? otail : doff;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst->k + 8 * (8 * wave)), 16, o, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst->v + 8 * (8 * wave)), 16, o, 0, 0, 0);
@@ -198,8 +217,8 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // when the constant (e/4)*8 + e%4 exceeds one per-lane threshold.
   auto mask_s = [&](int hh, f32x16& s) __attribute__((always_inline)) {
     const int k0 = hh * 32;
-    if (!((k0 + 32 > L) || (a.causal && k0 + 32 > qw0))) return;
-    const int last = a.causal ? min(qw0 + li, L - 1) : L - 1;
+    if (!((k0 + 32 > Lk) || (a.causal && k0 + 32 > qgw0))) return;
+    const int last = a.causal ? min(qgw0 + li, Lk - 1) : Lk - 1;
     const int d = last - k0 - 4 * lg;
 #pragma unroll
     for (int e = 0; e < 16; ++e)

@@ -37,20 +37,16 @@ static void fill_fwd_args(const Plan& pl, AttnFwdArgs* a) {
     a->L[i] = pl.L[i];
     a->nseg[i] = pl.nseg[i];
     a->nsp[i] = pl.N / pl.r[i];
+    a->Lk[i] = pl.Lk[i];
+    a->qoff[i] = pl.qoff[i];
   }
 }
 
-}  // namespace dla
-
-using namespace dla;
-
-extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const void* q,
-                           const void* k, const void* v, void* o, float* lse, void* ws,
-                           size_t ws_bytes, void* stream) {
-  clear_error();
-  Plan pl;
-  int rc = make_plan(desc, shape, &pl);
-  if (rc) return rc;
+// Attention pass and merge for a validated plan (whole sequence or shard).
+static int forward_impl(const Plan& pl, const void* q, const void* k, const void* v,
+                        const void* const* ext_k, const void* const* ext_v, void* o, float* lse,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int rc;
   if (pl.empty) return DLA_OK;  // nothing is read or written; pointers may be null
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
       (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")))
@@ -66,6 +62,14 @@ extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const v
   a.o = o;
   a.lse = lse;
   fill_fwd_args(pl, &a);
+  for (int i = 0; i < pl.P; ++i) {
+    if (!pl.span[i]) continue;
+    if (!ext_k || !ext_v) return fail(DLA_E_INVALID, "pattern %d spans shards: ext_k/ext_v are null", i);
+    if ((rc = check_ptr(ext_k[i], "ext_k[pattern]")) || (rc = check_ptr(ext_v[i], "ext_v[pattern]")))
+      return rc;
+    a.ext_k[i] = ext_k[i];
+    a.ext_v[i] = ext_v[i];
+  }
   for (int i = 0; i < pl.P; ++i) {
     if (i == pl.prim) continue;
     a.part_o[i] = (char*)ws + pl.part_o_off[i];
@@ -119,6 +123,62 @@ extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const v
     e = launch_combine(cb, pl.dtype, st);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
+  return DLA_OK;
+}
+
+}  // namespace dla
+
+using namespace dla;
+
+extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const void* q,
+                           const void* k, const void* v, void* o, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl);
+  if (rc) return rc;
+  return forward_impl(pl, q, k, v, nullptr, nullptr, o, lse, ws, ws_bytes, stream);
+}
+
+extern "C" int dla_forward_shard(const dla_desc* desc, const dla_shape* shape,
+                                 const dla_shard* shard, const void* q, const void* k,
+                                 const void* v, const void* const* ext_k,
+                                 const void* const* ext_v, void* o, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!shard) return fail(DLA_E_INVALID, "null shard");
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl, shard);
+  if (rc) return rc;
+  return forward_impl(pl, q, k, v, ext_k, ext_v, o, lse, ws, ws_bytes, stream);
+}
+
+extern "C" int dla_shard_gather(const dla_desc* desc, const dla_shape* shape,
+                                const dla_shard* shard, int32_t pattern, const void* x, void* out,
+                                void* stream) {
+  clear_error();
+  if (!shard) return fail(DLA_E_INVALID, "null shard");
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl, shard);
+  if (rc) return rc;
+  if (pattern < 0 || pattern >= pl.P)
+    return fail(DLA_E_INVALID, "pattern index %d outside 0..%d", pattern, pl.P - 1);
+  if (!pl.span[pattern])
+    return fail(DLA_E_INVALID, "pattern %d does not span shards (w <= N)", pattern);
+  if (pl.empty) return DLA_OK;
+  if ((rc = check_ptr(x, "x")) || (rc = check_ptr(out, "out"))) return rc;
+  ShardGatherArgs a{};
+  a.x = x;
+  a.out = out;
+  a.sb = pl.sb;
+  a.sn = pl.sn;
+  a.sh = pl.sh;
+  a.B = pl.B;
+  a.H = pl.H;
+  a.r = pl.r[pattern];
+  a.cr = pl.N / pl.r[pattern];
+  hipError_t e = launch_shard_gather(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "shard gather launch");
   return DLA_OK;
 }
 

@@ -24,6 +24,16 @@ struct AttnFwdArgs {
   int w[kMaxP], r[kMaxP], L[kMaxP];
   int64_t nseg[kMaxP];
   int64_t nsp[kMaxP];      // N / r: sparse rows per (batch, head) of each pattern
+  // Sequence shards: a pattern whose segments span several devices reads its
+  // keys and values from gathered buffers ext_k/ext_v laid out as
+  // [devices of the segment, B, H, nsp, D] (one chunk of nsp sparse rows per
+  // device, in segment order); its local query row i is row qoff + i of the
+  // segment, which has Lk key rows.  Otherwise Lk == L, qoff == 0 and the
+  // ext pointers are null.
+  int Lk[kMaxP];
+  int qoff[kMaxP];
+  const void* ext_k[kMaxP];
+  const void* ext_v[kMaxP];
   Schedule sched;
 };
 
@@ -44,6 +54,15 @@ struct CombineArgs {
   // rates share the set of patterns that keep them.
   uint32_t R;              // 0: per-row launch
   uint32_t rows_per_class; // N / R
+};
+
+// One device's part of the key/value exchange of a spanning pattern.
+struct ShardGatherArgs {
+  const void* x;           // k or v of the shard, [B, N, H, D] bf16 with strides sb/sn/sh
+  void* out;               // [B, H, cr, D] contiguous
+  int64_t sb, sn, sh;
+  int64_t B, H;
+  int64_t r, cr;           // rate, cr = N / r
 };
 
 struct RowMapArgs {
@@ -123,6 +142,7 @@ class TimedLaunch {
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream);
+hipError_t launch_shard_gather(const ShardGatherArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_row_map(const RowMapArgs& a, hipStream_t stream);

@@ -25,7 +25,7 @@ void clear_error() { g_err[0] = 0; }
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan) {
+int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dla_shard* shard) {
   if (!desc || !shape || !plan) return fail(DLA_E_INVALID, "null descriptor or shape");
   Plan& p = *plan;
   memset(&p, 0, sizeof(p));
@@ -63,22 +63,47 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan) {
   p.scale = desc->scale;
   p.empty = (p.B == 0 || p.H == 0);
 
+  int64_t total = p.N, start = 0;
+  if (shard) {
+    total = shard->total_rows;
+    start = shard->shard_start;
+    if (total < p.N || total % p.N)
+      return fail(DLA_E_INVALID, "total_rows=%lld is not a positive multiple of N=%lld",
+                  (long long)total, (long long)p.N);
+    if (start < 0 || start >= total || start % p.N)
+      return fail(DLA_E_INVALID, "shard_start=%lld is not a multiple of N=%lld below total_rows",
+                  (long long)start, (long long)p.N);
+    if (p.dtype != DLA_BF16) return fail(DLA_E_UNSUPPORTED, "sequence shards are implemented for bf16");
+  }
+  p.shard = shard != nullptr;
+
   for (int i = 0; i < p.P; ++i) {
     const int w = desc->patterns[i].w, r = desc->patterns[i].r;
     if (w < 1 || r < 1) return fail(DLA_E_INVALID, "pattern %d: w=%d r=%d must be >= 1", i, w, r);
     if (w % r) return fail(DLA_E_UNSUPPORTED, "pattern %d: r=%d does not divide w=%d", i, r, w);
-    if (w > p.N) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d exceeds N=%lld", i, w,
-                             (long long)p.N);
-    if (p.N % w) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d does not divide N=%lld", i, w,
-                             (long long)p.N);
+    if (w > total) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d exceeds N=%lld", i, w,
+                               (long long)total);
+    if (total % w) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d does not divide N=%lld", i, w,
+                               (long long)total);
+    const bool spans = w > p.N;  // only with a shard: w <= total
+    if (!spans && p.N % w)
+      return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d does not divide the shard length N=%lld", i,
+                  w, (long long)p.N);
+    if (spans && (w % p.N || p.N % r || (p.N / r) % 64))
+      return fail(DLA_E_UNSUPPORTED,
+                  "pattern %d: a segment (w=%d) spanning shards of N=%lld rows needs N | w, r | N "
+                  "and 64 | N/r (r=%d)", i, w, (long long)p.N, r);
     // The backward streams 64 dilated rows per tile through one 32-bit
     // buffer offset range.
     if ((int64_t)64 * r * shape->stride_n * (shape->dtype == DLA_F32 ? 4 : 2) + 128 > INT32_MAX)
       return fail(DLA_E_UNSUPPORTED, "pattern %d: 64 dilated rows span more than 2 GiB", i);
     p.w[i] = w;
     p.r[i] = r;
-    p.L[i] = w / r;
-    p.nseg[i] = p.N / w;
+    p.span[i] = spans;
+    p.Lk[i] = w / r;
+    p.L[i] = spans ? (int)(p.N / r) : w / r;
+    p.qoff[i] = spans ? (int)((start % w) / r) : 0;
+    p.nseg[i] = spans ? 1 : p.N / w;
   }
 
   // The pattern that keeps the most rows (smallest r, first on ties) writes
@@ -121,8 +146,20 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan) {
   for (int i = 0; i < p.P; ++i) {
     const int64_t L = p.L[i];
     int64_t per = 0, seg_pairs = 0;
-    ovf |= __builtin_mul_overflow(L, p.causal ? L + 1 : L, &per);
-    if (p.causal) per /= 2;
+    if (p.span[i]) {
+      // local queries qoff .. qoff+L-1 of a segment with Lk keys
+      if (p.causal) {
+        int64_t head = 0;
+        ovf |= __builtin_mul_overflow(L, (int64_t)p.qoff[i], &head);
+        per = L * (L + 1) / 2;
+        ovf |= __builtin_add_overflow(per, head, &per);
+      } else {
+        ovf |= __builtin_mul_overflow(L, (int64_t)p.Lk[i], &per);
+      }
+    } else {
+      ovf |= __builtin_mul_overflow(L, p.causal ? L + 1 : L, &per);
+      if (p.causal) per /= 2;
+    }
     ovf |= __builtin_mul_overflow(p.nseg[i], per, &seg_pairs);
     ovf |= __builtin_add_overflow(pairs, seg_pairs, &pairs);
   }
@@ -172,6 +209,27 @@ int dla_plan_check(const dla_desc* desc, const dla_shape* shape, size_t* ws_fwd_
   if (rc != DLA_OK) return rc;
   if (ws_fwd_bytes) *ws_fwd_bytes = p.ws_fwd;
   if (ws_bwd_bytes) *ws_bwd_bytes = p.ws_bwd;
+  return DLA_OK;
+}
+
+int dla_plan_check_shard(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
+                         size_t* ws_fwd_bytes) {
+  if (!shard) return dla::fail(DLA_E_INVALID, "null shard");
+  dla::Plan p;
+  const int rc = dla::make_plan(desc, shape, &p, shard);
+  if (rc != DLA_OK) return rc;
+  if (ws_fwd_bytes) *ws_fwd_bytes = p.ws_fwd;
+  return DLA_OK;
+}
+
+int dla_pair_count_shard(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
+                         int64_t* pairs) {
+  if (!shard) return dla::fail(DLA_E_INVALID, "null shard");
+  dla::Plan p;
+  const int rc = dla::make_plan(desc, shape, &p, shard);
+  if (rc != DLA_OK) return rc;
+  if (!pairs) return dla::fail(DLA_E_INVALID, "null output pointer");
+  *pairs = p.pairs;
   return DLA_OK;
 }
 

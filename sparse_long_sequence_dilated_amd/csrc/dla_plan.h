@@ -38,6 +38,13 @@ struct Plan {
   float scale;
   int w[kMaxP], r[kMaxP], L[kMaxP];
   int64_t nseg[kMaxP];
+  // Sequence shard (dla_forward_shard): a pattern whose segments are longer
+  // than the shard spans devices; the shard holds L = N/r of its Lk = w/r
+  // sparse rows, starting at sparse row qoff of one segment (nseg = 1).
+  bool shard;
+  bool span[kMaxP];
+  int Lk[kMaxP];                // key rows per segment (== L unless spanning)
+  int qoff[kMaxP];              // segment row of local sparse row 0 (0 unless spanning)
   int prim;                     // pattern whose result goes straight to o/lse
   bool need_combine;            // a merge pass is needed after the attention pass
   bool empty;                   // B == 0 or H == 0: nothing to do
@@ -55,9 +62,11 @@ struct Plan {
   int64_t pairs;
 };
 
-// Validate and fill `plan`.  Returns DLA_OK or an error code; the message is
-// recorded for dla_last_error().
-int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan);
+// Validate and fill `plan` (for one shard of a longer sequence when `shard`
+// is not null).  Returns DLA_OK or an error code; the message is recorded for
+// dla_last_error().
+int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan,
+              const dla_shard* shard = nullptr);
 
 // Fill `s` for tiles of `tile_rows` sparse rows per unit.
 void make_schedule(const Plan& plan, int tile_rows, Schedule* s);

@@ -25,6 +25,7 @@ MAX_PATTERNS = 16
 HEAD_DIM = 64
 
 EXPORTS = ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
+           "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather", "dla_forward_shard",
            "dla_timing_enable", "dla_timing_collect", "dla_strerror", "dla_last_error")
 
 
@@ -49,6 +50,10 @@ class Shape(ctypes.Structure):
                 ("stride_n", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
 
 
+class Shard(ctypes.Structure):
+    _fields_ = [("total_rows", ctypes.c_int64), ("shard_start", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -68,6 +73,12 @@ def lib():
     L.dla_backward.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dla_row_map.argtypes = [pd, i64, i32, i32, vp, vp]
     L.dla_pair_count.argtypes = [pd, ps, ctypes.POINTER(i64)]
+    psh = ctypes.POINTER(Shard)
+    L.dla_plan_check_shard.argtypes = [pd, ps, psh, ctypes.POINTER(sz)]
+    L.dla_pair_count_shard.argtypes = [pd, ps, psh, ctypes.POINTER(i64)]
+    L.dla_shard_gather.argtypes = [pd, ps, psh, i32, vp, vp, vp]
+    L.dla_forward_shard.argtypes = [pd, ps, psh, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                    vp, vp, vp, sz, vp]
     L.dla_timing_enable.argtypes = [ctypes.c_int]
     L.dla_timing_enable.restype = ctypes.c_int
     L.dla_timing_collect.argtypes = [ctypes.c_char_p, ctypes.POINTER(i64),
@@ -77,7 +88,9 @@ def lib():
     L.dla_strerror.restype = ctypes.c_char_p
     L.dla_last_error.argtypes = []
     L.dla_last_error.restype = ctypes.c_char_p
-    for name in ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count"):
+    for name in ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
+                 "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather",
+                 "dla_forward_shard"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -237,3 +250,94 @@ def row_map(patterns, N, H, pattern, device="cuda", stream=None):
     _check(lib().dla_row_map(ctypes.byref(desc), N, H, pattern, out.data_ptr(),
                              _stream(stream, out.device)))
     return out
+
+
+# ---- sequence shards (one device's share of the sequence-split scheme) ----
+
+def plan_check_shard(patterns, causal, scale, B, N, H, total_rows, shard_start, D=HEAD_DIM,
+                     dtype=DLA_BF16, strides=None):
+    """Forward workspace bytes of one shard; raises DlaError on an invalid shard."""
+    d = make_desc(patterns, causal, scale)
+    s = make_shape(B, N, H, D, dtype, strides)
+    sh = Shard(total_rows, shard_start)
+    f = ctypes.c_size_t(0)
+    _check(lib().dla_plan_check_shard(ctypes.byref(d), ctypes.byref(s), ctypes.byref(sh), ctypes.byref(f)))
+    return f.value
+
+
+def plan_check_shard_code(patterns, causal, scale, B, N, H, total_rows, shard_start, D=HEAD_DIM,
+                          dtype=DLA_BF16):
+    """Raw return code of dla_plan_check_shard (for error-path tests)."""
+    d = make_desc(patterns, causal, scale)
+    s = make_shape(B, N, H, D, dtype)
+    sh = Shard(total_rows, shard_start)
+    return lib().dla_plan_check_shard(ctypes.byref(d), ctypes.byref(s), ctypes.byref(sh), None)
+
+
+def pair_count_shard(patterns, causal, B, N, H, total_rows, shard_start):
+    d = make_desc(patterns, causal, 1.0)
+    s = make_shape(B, N, H, HEAD_DIM, DLA_BF16)
+    sh = Shard(total_rows, shard_start)
+    out = ctypes.c_int64(0)
+    _check(lib().dla_pair_count_shard(ctypes.byref(d), ctypes.byref(s), ctypes.byref(sh), ctypes.byref(out)))
+    return out.value
+
+
+def shard_gather(x, patterns, pattern, total_rows, shard_start, causal=True, out=None, stream=None):
+    """This shard's part of the exchange of spanning pattern `pattern`: [B, H, N/r, D]."""
+    import torch
+    shape = _shape_of(x)
+    desc = make_desc(patterns, causal, 1.0)
+    sh = Shard(total_rows, shard_start)
+    B, N, H, D = x.shape
+    r = patterns[pattern][1]
+    if out is None:
+        out = torch.empty((B, H, N // r, D), dtype=x.dtype, device=x.device)
+    if out.shape != (B, H, N // r, D) or not out.is_contiguous() or out.dtype != x.dtype:
+        raise DlaError(DLA_E_INVALID, "out must be a contiguous [B, H, N/r, D] tensor of x's dtype")
+    _check(lib().dla_shard_gather(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(sh), pattern,
+                                  x.data_ptr(), out.data_ptr(), _stream(stream, x.device)))
+    return out
+
+
+def forward_shard(q, k, v, patterns, total_rows, shard_start, ext_k=None, ext_v=None, causal=True,
+                  scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Forward pass of one shard; returns (o, lse) for the shard's rows.
+
+    ext_k / ext_v: dicts {pattern index: [w/N, B, H, N/r, D] gathered tensor}
+    for the patterns whose segments span shards.
+    """
+    import torch
+    scale = default_scale(q.shape[-1]) if scale is None else scale
+    _same_layout(q, k, v)
+    shape = _shape_of(q)
+    desc = make_desc(patterns, causal, scale)
+    sh = Shard(total_rows, shard_start)
+    ws_f = ctypes.c_size_t(0)
+    _check(lib().dla_plan_check_shard(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(sh),
+                                      ctypes.byref(ws_f)))
+    B, N, H, _ = q.shape
+    o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
+    _same_layout(q, o)
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if lse_t.shape != (B, H, N) or not lse_t.is_contiguous() or lse_t.dtype != torch.float32:
+        raise DlaError(DLA_E_INVALID, "lse must be a contiguous float32 [B, H, N] tensor")
+    P = len(patterns)
+    ek = (ctypes.c_void_p * P)()
+    ev = (ctypes.c_void_p * P)()
+    for i, (w, r) in enumerate(patterns):
+        if w > N:
+            tk, tv = (ext_k or {}).get(i), (ext_v or {}).get(i)
+            want = (w // N, B, H, N // r, q.shape[-1])
+            for t in (tk, tv):
+                if t is None or tuple(t.shape) != want or not t.is_contiguous() or t.dtype != q.dtype:
+                    raise DlaError(DLA_E_INVALID, f"pattern {i} spans shards: needs contiguous "
+                                   f"gathered k and v of shape {want}")
+            ek[i], ev[i] = tk.data_ptr(), tv.data_ptr()
+    if workspace is None:
+        workspace = torch.empty(max(ws_f.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().dla_forward_shard(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(sh),
+                                   q.data_ptr(), k.data_ptr(), v.data_ptr(), ek, ev, o.data_ptr(),
+                                   lse_t.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   _stream(stream, q.device)))
+    return o, lse_t

@@ -1,0 +1,122 @@
+"""GPU parity of sequence shards (needs an MI355X).
+
+One device's share of the sequence-split scheme (the gptget.net LongNet
+summary, section 方法论, distributed item): the sequence of total_rows rows is
+cut into G shards of N rows; a segment longer than a shard spans devices, and
+its sparsified keys and values are exchanged.  Here every device is played by
+slices of one tensor on one GPU: each shard's part of the exchange comes from
+dla_shard_gather on that shard's slice, the parts of a segment's devices are
+stacked in device order (what an all-gather returns), and dla_forward_shard
+must reproduce the oracle's result for the whole sequence on the shard's
+rows.  Every call goes through the C ABI.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_long_sequence_dilated_amd import dla, inputs
+from tests.gpu_util import TOL, normwise, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gathered(x, pats, p, N, total, g):
+    """[w/N, B, H, N/r, D]: the parts of the devices of shard g's segment."""
+    import torch
+    w = pats[p][0]
+    s = (g * N) // w
+    parts = []
+    for gd in range(s * w // N, (s + 1) * w // N):
+        parts.append(dla.shard_gather(x[:, gd * N:(gd + 1) * N], pats, p, total, gd * N))
+    return torch.stack(parts).contiguous()
+
+
+def _run_shards(tq, tk, tv, pats, causal, scale, N, total):
+    import torch
+    outs, lses = [], []
+    for g in range(total // N):
+        ext_k, ext_v = {}, {}
+        for p, (w, r) in enumerate(pats):
+            if w > N:
+                ext_k[p] = _gathered(tk, pats, p, N, total, g)
+                ext_v[p] = _gathered(tv, pats, p, N, total, g)
+        sl = slice(g * N, (g + 1) * N)
+        o, lse = dla.forward_shard(tq[:, sl], tk[:, sl], tv[:, sl], pats, total, g * N, ext_k, ext_v,
+                                   causal, scale)
+        outs.append(o)
+        lses.append(lse)
+    torch.cuda.synchronize()
+    return torch.cat(outs, dim=1), torch.cat(lses, dim=2)
+
+
+def test_shard_gather_is_exact():
+    import torch
+    B, N, H, total = 2, 512, 3, 2048
+    pats = ((256, 1), (1024, 4), (2048, 4))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    x = torch.randn((B, total, H, 64), device="cuda", generator=g).bfloat16()
+    for p in (1, 2):
+        r = pats[p][1]
+        for gd in range(total // N):
+            xs = x[:, gd * N:(gd + 1) * N]
+            got = dla.shard_gather(xs, pats, p, total, gd * N)
+            want = torch.stack([xs[:, (h % r)::r, h, :] for h in range(H)], dim=1)
+            assert torch.equal(got, want), (p, gd)
+
+
+CASES = [
+    # (B, total, H, patterns, causal, G)
+    (2, 2048, 3, ((256, 1), (1024, 4), (2048, 4)), True, 4),
+    (2, 2048, 3, ((256, 1), (1024, 4), (2048, 4)), False, 4),
+    (1, 2048, 2, ((256, 1), (1024, 4), (2048, 4)), True, 8),      # N/r = 64: one tile per chunk
+    (1, 4096, 3, ((512, 1), (4096, 2)), True, 2),                 # r = 1 local, two-device segment
+    (1, 2048, 2, ((2048, 1),), True, 4),                          # one spanning pattern, r = 1
+    (1, 2048, 13, ((2048, 4), (1024, 2)), True, 4),               # every pattern spans; uncovered rows
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}G{c[5]}-"
+                         f"{'c' if c[4] else 'nc'}-{'_'.join(f'{w}x{r}' for w, r in c[3])}")
+def test_forward_shards_match_whole_sequence_oracle(case):
+    B, total, H, pats, causal, G = case
+    N = total // G
+    seed = sum(ord(ch) for ch in str(case))
+    q, k, v = inputs.random_case(seed, B, total, H, "bf16")
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    o, lse = _run_shards(tq, tk, tv, pats, causal, 0.125, N, total)
+    o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, 0.125)
+    eo, el = normwise(to_host(o), o_ref), normwise(to_host(lse), lse_ref)
+    print(f"{case}: O {eo:.3e} LSE {el:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+def test_forward_shard_c4_eight_way_last_shard_sampled_rows():
+    """C4 split over 8 devices: the last shard (patterns i = 7..9 span 2, 4, 8 devices)."""
+    import torch
+    wl = inputs.WORKLOADS["C4"]
+    total, G = wl.N, 8
+    N = total // G
+    q, k, v = inputs.workload_inputs(wl)
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    g = G - 1
+    ext_k, ext_v = {}, {}
+    for p, (w, r) in enumerate(wl.patterns):
+        if w > N:
+            ext_k[p] = _gathered(tk, wl.patterns, p, N, total, g)
+            ext_v[p] = _gathered(tv, wl.patterns, p, N, total, g)
+    sl = slice(g * N, (g + 1) * N)
+    o, lse = dla.forward_shard(tq[:, sl], tk[:, sl], tv[:, sl], wl.patterns, total, g * N,
+                               ext_k, ext_v, True, wl.scale)
+    torch.cuda.synchronize()
+    del tq, tk, tv, ext_k, ext_v
+    rng = np.random.default_rng(11)
+    special = np.array([0, 1, 255, 256, N // 2, N - 2, N - 1])
+    for h in (0, 7, 11):
+        local = np.unique(np.concatenate([special, rng.integers(0, N, 41)]))
+        o_ref, l_ref = oracle.forward_rows(q, k, v, wl.patterns, True, wl.scale, 0, h, g * N + local)
+        idx = torch.from_numpy(local).cuda()
+        eo = normwise(o[0, :, h][idx].float().cpu().numpy(), o_ref)
+        el = normwise(lse[0, h][idx].cpu().numpy(), l_ref)
+        print(f"C4 shard {g}/{G} head {h}: O {eo:.3e} LSE {el:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"]
