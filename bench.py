@@ -10,6 +10,9 @@ settings of the gptget.net LongNet summary, section 实验设计, at 32K tokens)
 
 Also reported, as extra fields of the same line:
   * forward-only throughput at N=32768 (B=1) and N=1,048,576 (B=1);
+  * `shard_forward`: one device's share when the 1M-token sequence is split
+    over 8 devices (the last shard, whose segments of the three coarsest
+    patterns span 2, 4 and 8 devices): its exchange parts and its forward;
   * `roofline` of the kernel family that takes most of the timed region,
     timed live with HIP events around its launches on the launch stream;
   * `cpu_baseline`: the CPU oracle (float32, thread pool) on a bounded
@@ -122,7 +125,8 @@ def time_steps(step, steps, warmup):
     t1 = time.perf_counter()
     dla.timing_enable(False)
     fams = {}
-    for fam in ("attn_fwd", "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd", "bwd_finalize"):
+    for fam in ("attn_fwd", "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd", "bwd_finalize",
+                "shard_gather"):
         n, ms = dla.timing_collect(fam)
         if n:
             fams[fam] = (n, ms)
@@ -150,6 +154,52 @@ def forward_only(name, steps, warmup):
     for fam, (n, fms) in fams.items():
         out[f"{fam}_us_per_launch"] = 1e3 * fms / n
     del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def shard_forward(name, devices, shard, steps, warmup):
+    """One device's share of the sequence-split scheme: workload `name` cut into
+    `devices` shards, the work of shard `shard` (its parts of the key/value
+    exchange, then the shard's forward against the gathered segments).  The
+    collective between the two is not part of a one-GPU step."""
+    import torch
+    from sparse_long_sequence_dilated_amd import dla, inputs
+    wl = inputs.WORKLOADS[name]
+    N = wl.N // devices
+    start = shard * N
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2000 + wl.seed)
+    q, k, v = (torch.randn((wl.B, N, wl.H, wl.D), device="cuda", generator=g).bfloat16() for _ in range(3))
+    span = [i for i, (w, r) in enumerate(wl.patterns) if w > N]
+    ext_k = {i: torch.randn((wl.patterns[i][0] // N, wl.B, wl.H, N // wl.patterns[i][1], wl.D),
+                            device="cuda", generator=g).bfloat16() for i in span}
+    ext_v = {i: torch.randn_like(ext_k[i]) for i in span}
+    part_k = {i: torch.empty((wl.B, wl.H, N // wl.patterns[i][1], wl.D), dtype=torch.bfloat16,
+                             device="cuda") for i in span}
+    part_v = {i: torch.empty_like(part_k[i]) for i in span}
+    ws_f = dla.plan_check_shard(wl.patterns, wl.causal, wl.scale, wl.B, N, wl.H, wl.N, start)
+    ws = torch.empty(max(ws_f, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        for i in span:
+            dla.shard_gather(k, wl.patterns, i, wl.N, start, wl.causal, out=part_k[i])
+            dla.shard_gather(v, wl.patterns, i, wl.N, start, wl.causal, out=part_v[i])
+        dla.forward_shard(q, k, v, wl.patterns, wl.N, start, ext_k, ext_v, wl.causal, wl.scale,
+                          out=o, lse=lse, workspace=ws)
+
+    ms, fams = time_steps(step, steps, warmup)
+    pairs = dla.pair_count_shard(wl.patterns, wl.causal, wl.B, N, wl.H, wl.N, start)
+    tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
+    out = {"workload": f"{wl.describe()}, split over {devices} devices, shard {shard} "
+                       f"(rows {start}..{start + N - 1}; {len(span)} patterns span devices)",
+           "tokens_per_s": wl.B * N / (ms * 1e-3), "ms": ms, "useful_tflops": tflops,
+           "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS}
+    for fam, (n, fms) in fams.items():
+        out[f"{fam}_us_per_launch"] = 1e3 * fms / n
+    del q, k, v, o, lse, ws, ext_k, ext_v, part_k, part_v
     torch.cuda.empty_cache()
     return out
 
@@ -253,6 +303,7 @@ def main():
     if not args.no_forward_lines:
         extra.append(forward_only("C3", max(5, args.steps), args.warmup))
         extra.append(forward_only("C4", max(3, args.steps // 4), 1))
+        shard = shard_forward("C4", 8, 7, max(3, args.steps // 2), 1)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
     line = {
@@ -265,6 +316,8 @@ def main():
         "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
         "roofline": roofline, "kernels": kernels, "forward_only": extra, "cpu_baseline": cpu,
     }
+    if not args.no_forward_lines:
+        line["shard_forward"] = shard
     print(json.dumps(line), flush=True)
 
 
