@@ -55,6 +55,9 @@ struct __align__(16) FwdStage {
   uint4 v[kFwdBN * 8];  // 8 KB
 };
 
+// kShard: some pattern reads gathered keys (a sequence shard); the plain
+// instantiation has none of that logic.
+template <bool kShard>
 __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs a) {
   __shared__ FwdStage ring[kStages];
   const int tid = threadIdx.x;
@@ -68,12 +71,13 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // L query rows (local), Lk key rows; local query row i is row qoff + i of
   // the segment (qoff = 0 and Lk = L except for a segment that spans
   // several sequence shards, whose keys come from the gathered buffers).
-  const int w = a.w[p], r = a.r[p], L = a.L[p], Lk = a.Lk[p], qoff = a.qoff[p];
+  const int w = a.w[p], r = a.r[p], L = a.L[p];
+  const int Lk = kShard ? a.Lk[p] : L, qoff = kShard ? a.qoff[p] : 0;
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const int64_t rstride = (int64_t)r * a.sn;  // elements between consecutive sparse rows
   const __bf16* Qh = (const __bf16*)a.q + head_off + base_row * a.sn;
-  const bool ext = a.ext_k[p] != nullptr;
+  const bool ext = kShard && a.ext_k[p] != nullptr;
   const int64_t cr = a.nsp[p];                 // rows per gathered chunk
   const __bf16* Kh = ext ? (const __bf16*)a.ext_k[p] + ((int64_t)b * a.H + h) * cr * kD
                          : (const __bf16*)a.k + head_off + base_row * a.sn;
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vcur, span);
     kcur += tile_bytes;
     vcur += tile_bytes;
-    if (++tc == tiles_per_chunk) {
+    if (kShard && ++tc == tiles_per_chunk) {
       tc = 0;
       kcur += chunk_jump;
       vcur += chunk_jump;
@@ -372,9 +376,15 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream) {
   if (a.sched.total == 0) return hipSuccess;
+  bool shard = false;
+  for (int i = 0; i < a.P; ++i) shard |= a.ext_k[i] != nullptr;
   TimedLaunch tl("attn_fwd", stream);
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)a.sched.total), dim3(64 * kFwdWaves), 0,
-                     stream, a);
+  if (shard)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)a.sched.total), dim3(64 * kFwdWaves),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)a.sched.total), dim3(64 * kFwdWaves),
+                       0, stream, a);
   return hipGetLastError();
 }
 
