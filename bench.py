@@ -178,7 +178,7 @@ def shard_forward(name, devices, shard, steps, warmup):
     part_k = {i: torch.empty((wl.B, wl.H, N // wl.patterns[i][1], wl.D), dtype=torch.bfloat16,
                              device="cuda") for i in span}
     part_v = {i: torch.empty_like(part_k[i]) for i in span}
-    ws_f = dla.plan_check_shard(wl.patterns, wl.causal, wl.scale, wl.B, N, wl.H, wl.N, start)
+    ws_f, _ = dla.plan_check_shard(wl.patterns, wl.causal, wl.scale, wl.B, N, wl.H, wl.N, start)
     ws = torch.empty(max(ws_f, 1), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((wl.B, wl.H, N), dtype=torch.float32, device="cuda")

@@ -161,11 +161,12 @@ typedef struct {
 
 /*
  * Validate a descriptor, a shard shape and its place in the sequence on the
- * host and report the workspace bytes dla_forward_shard needs (the out
- * pointer may be NULL).  Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
+ * host and report the workspace bytes dla_forward_shard and
+ * dla_backward_shard need (either out pointer may be NULL).
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
  */
 int dla_plan_check_shard(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
-                         size_t* ws_fwd_bytes);
+                         size_t* ws_fwd_bytes, size_t* ws_bwd_bytes);
 
 /*
  * Number of (query, key) pairs the shard evaluates: the pairs of
@@ -207,12 +208,53 @@ int dla_forward_shard(const dla_desc* desc, const dla_shape* shape, const dla_sh
                       void* stream);
 
 /*
+ * Backward pass of one shard, first half.  (o, lse) are the shard's outputs
+ * of dla_forward_shard, dout its upstream gradient, ext_k/ext_v the same
+ * gathered segments.  Writes:
+ *   - dq for every row of the shard (bf16, final);
+ *   - dk, dv for the shard's rows that no spanning pattern keeps (final);
+ *   - for every spanning pattern p, ext_dk[p] and ext_dv[p]: this shard's
+ *     contributions to the gradients of the whole segment's sparsified keys
+ *     and values, fp32 [w_p/N, B, H, N/r_p, D] in the exchange layout (device
+ *     order), already scaled.  The caller sums them over the devices of the
+ *     segment and hands each device its part (a reduce-scatter), then calls
+ *     dla_shard_finish.
+ * The workspace (dla_plan_check_shard's backward size) carries the local
+ * patterns' partial gradients to dla_shard_finish and must not change in
+ * between.  The backward also needs N / r_p to be a multiple of 128 for
+ * every spanning pattern (DLA_E_UNSUPPORTED otherwise).
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_WORKSPACE, DLA_E_HIP.
+ */
+int dla_backward_shard(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
+                       const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, const void* const* ext_k,
+                       const void* const* ext_v, void* dq, void* dk, void* dv,
+                       void* const* ext_dk, void* const* ext_dv, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Backward pass of one shard, second half: for every row of the shard that
+ * a spanning pattern keeps, dk and dv become the sum of the local patterns'
+ * partials (from the workspace) and, for each spanning pattern p, the
+ * exchanged part red_dk[p] / red_dv[p] (fp32 [B, H, N/r_p, D]: the sum over
+ * the segment's devices of their ext_dk[p] / ext_dv[p] parts for this
+ * shard), rounded once.  Other rows are left as dla_backward_shard wrote
+ * them.  The arrays are host memory with num_patterns entries (entries of
+ * local patterns are ignored).
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_WORKSPACE, DLA_E_HIP.
+ */
+int dla_shard_finish(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
+                     const float* const* red_dk, const float* const* red_dv, void* dk, void* dv,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Opt-in launch timing, a profiling aid.  While enabled (on != 0), every
  * kernel launch made by dla_forward / dla_backward is bracketed by two HIP
  * events recorded on the caller's stream (host-side bookkeeping only; the
  * kernels are unchanged).  Kernel families: "attn_fwd" (bf16 forward
  * attention), "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd",
- * "bwd_finalize", "shard_gather".
+ * "bwd_finalize", "shard_gather" (a shard's exchange parts and
+ * relayouts), "shard_finish".
  */
 int dla_timing_enable(int on);
 

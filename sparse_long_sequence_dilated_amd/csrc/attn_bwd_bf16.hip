@@ -60,8 +60,10 @@ __device__ __forceinline__ bf16x8 words_bf16(const uint32_t (&w)[8], int half) {
   return __builtin_bit_cast(bf16x8, uint4{w[4 * half], w[4 * half + 1], w[4 * half + 2], w[4 * half + 3]});
 }
 
-// kKV: key unit (dK, dV) or query unit (dQ).
-template <bool kKV>
+// kKV: key unit (dK, dV) or query unit (dQ).  kWin: the launch covers a
+// window [qlo, qhi) of a segment's query rows (one sequence shard's queries
+// against a gathered segment); every result is then an fp32 partial.
+template <bool kKV, bool kWin>
 __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, int p, int b, int h,
                                          int64_t seg, int tile) {
   constexpr int kIns = kKV ? 5 : 4;  // DMA instructions per tile and wave
@@ -85,6 +87,8 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   const int own0 = tile * kBwdRows + 32 * wave;
   const int own = own0 + li;
   const bool wave_valid = own0 < L;
+  const int qlo = kWin ? a.qlo : 0, qhi = kWin ? a.qhi : L;  // query rows that exist
+  const int send = kKV ? qhi : L;                    // end of the streamed rows
   const __bf16* srcA = kKV ? Qh : Kh;   // streamed tensors
   const __bf16* srcB = kKV ? Dh : Vh;
   const __bf16* ownA = kKV ? Kh : Qh;   // owned tensors (B operands)
@@ -112,9 +116,10 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   int t_first, nt, h_lo, h_hi;
   if (kKV) {
     t_first = a.causal ? 2 * tile : 0;                 // queries >= the first owned key
-    nt = (L + kBwdTile - 1) / kBwdTile - t_first;
-    h_lo = a.causal ? wave : 0;                        // first half with a query >= own0
-    h_hi = (L - kBwdTile * t_first + 31) / 32;
+    if (kWin) t_first = max(t_first, qlo / kBwdTile);
+    nt = (send + kBwdTile - 1) / kBwdTile - t_first;
+    h_lo = a.causal ? max(0, own0 - kBwdTile * t_first) / 32 : 0;  // first half with a query >= own0
+    h_hi = (send - kBwdTile * t_first + 31) / 32;
   } else {
     t_first = 0;
     const int kend = a.causal ? min(L, tile * kBwdRows + kBwdRows) : L;
@@ -128,7 +133,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   auto need_mask = [&](int hh) __attribute__((always_inline)) {
     const int s0 = kBwdTile * t_first + 32 * hh;
     const bool diag = a.causal && (kKV ? own0 + 31 > s0 : s0 + 31 > own0);
-    return diag || (s0 + 32 > L) || (own0 + 32 > L);
+    return diag || (s0 + 32 > send) || (own0 + 32 > L);
   };
 
   // ---- HBM -> LDS: wave w fills rows [16w, 16w+16) of a tile, 8 rows per
@@ -147,7 +152,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   const uint32_t ld_voff = (uint32_t)(16 * wave + (lane >> 1)) * (uint32_t)(8 * r) + 4u * (lane & 1);
   auto issue_tile = [&](int t, BwdStage* __restrict__ dst) __attribute__((always_inline)) {
     const int trow0 = kBwdTile * (t_first + t);
-    const int lim = L - 1 - trow0;                      // last valid row of the tile
+    const int lim = send - 1 - trow0;                   // last valid row of the tile
     const __amdgpu_buffer_rsrc_t ra = buf_rsrc(srcA + (int64_t)trow0 * rstride, span);
     const __amdgpu_buffer_rsrc_t rb = buf_rsrc(srcB + (int64_t)trow0 * rstride, span);
     uint32_t vo[2] = {voff[0], voff[1]};
@@ -223,7 +228,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, -l2[i]));
         if (masked) {
           const int srow = s0 + 8 * g + 4 * lg + i;
-          const bool dead = kKV ? (srow >= L || own >= L || (a.causal && own > srow))
+          const bool dead = kKV ? (srow >= send || own >= L || (a.causal && own > srow))
                                 : (srow >= L || own >= L || (a.causal && srow > own));
           if (dead) p = 0.f;
         }
@@ -380,7 +385,10 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     else DLA_BWD_PHASE(2 * j + 1, 1, sc, sn, sc, sy, py, sx, px, pwy, swy, pwx, swx);
   };
 
-  // Prologue: tiles 0..2 in flight, wait for tile 0, S/dP of half 0.
+  // Prologue: tiles 0..2 in flight, wait for tile 0, S/dP of half 0.  (In a
+  // query window, a key tile past every query streams nothing and writes
+  // zeros.)
+  if (!kWin || nt > 0) {
   issue_tile(0, &ring[0]);
   if (nt > 1) issue_tile(1, &ring[1]);
   if (nt > 2) issue_tile(2, &ring[2]);
@@ -401,6 +409,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     ring_step(j, &ring[(j + 3) & 3], &ring[j & 3], &ring[(j + 1) & 3], &ring[(j + 3) & 3]);
   // Drain: gradient products of the last half.
   if (active(2 * nt - 1)) stage_grad(&ring[(nt - 1) & 3], 1, pwy, swy);
+  }
 #undef DLA_BWD_PHASE
 #undef DLA_DEAD
   (void)kIns;
@@ -430,14 +439,17 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     put(0, acc0, a.scale);
     if (kKV) put(1, acc1, 1.f);
     const int cc = lane & 15;
-    const int64_t part_row0 = ((int64_t)b * a.H + h) * a.nsp[p] + seg * L + own0;
+    // (a window's dQ partial holds the window's rows only: nsp_q rows per
+    // (batch, head), its base shifted back by qlo rows by the caller)
+    const int64_t nsp = (kWin && !kKV) ? a.nsp_q : a.nsp[p];
+    const int64_t part_row0 = ((int64_t)b * a.H + h) * nsp + seg * L + own0;
 #pragma unroll 2
     for (int it = 0; it < 8; ++it) {
       const int rr = 4 * it + (lane >> 4);
       const int ownr = own0 + rr;
       if (ownr >= L) continue;
       const int n = (int)base_row + ownr * r;
-      const bool shared = kept_count(a, n, h) > 1;
+      const bool shared = kWin || kept_count(a, n, h) > 1;
       const int64_t out_off = head_off + (int64_t)n * a.sn + 4 * cc;
       const int64_t part_off = (part_row0 + rr) * kD + 4 * cc;
 #pragma unroll
@@ -455,6 +467,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   }
 }
 
+template <bool kWin>
 __global__ __launch_bounds__(256, 2) void attn_bwd_bf16_kernel(const AttnBwdArgs a) {
   __shared__ BwdStage ring[kBwdStages];
   // Longest first: the schedules hand out the highest tile index first, which
@@ -470,9 +483,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_bf16_kernel(const AttnBwdArgs
               p, b, h, seg, tile);
   if (kv) {
     if (a.causal) tile = (a.L[p] + kBwdRows - 1) / kBwdRows - 1 - tile;
-    bwd_unit<true>(a, ring, p, b, h, seg, tile);
+    bwd_unit<true, kWin>(a, ring, p, b, h, seg, tile);
   } else {
-    bwd_unit<false>(a, ring, p, b, h, seg, tile);
+    if (kWin) tile += a.qlo / kBwdRows;                // the window's query tiles
+    bwd_unit<false, kWin>(a, ring, p, b, h, seg, tile);
   }
 }
 
@@ -480,7 +494,10 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
   const int64_t total = a.sched_kv.total + a.sched_q.total;
   if (total == 0) return hipSuccess;
   TimedLaunch tl("attn_bwd", stream);
-  hipLaunchKernelGGL(attn_bwd_bf16_kernel, dim3((unsigned)total), dim3(256), 0, stream, a);
+  if (a.qhi > 0)
+    hipLaunchKernelGGL(attn_bwd_bf16_kernel<true>, dim3((unsigned)total), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_bf16_kernel<false>, dim3((unsigned)total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -106,10 +106,14 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdFinalizeArgs
     kept |= (uint32_t)k << p;
     cnt += k;
   }
-  if (cnt < 2) return;
+  // Sequence shard: a row that a spanning pattern keeps has that pattern's
+  // dQ partial (finalized here even when no other pattern keeps it) but
+  // not its dK/dV, which the shard finish pass adds after the exchange.
+  const bool span = (kept & a.span_mask) != 0;
+  if (cnt < 2 && !span) return;
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t out_off = (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
-  for (int g = 0; g < 3; ++g) {
+  for (int g = 0; g < (span ? 1 : 3); ++g) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < a.P; ++p) {
       const bool k = (kept >> p) & 1;
@@ -141,7 +145,8 @@ __global__ __launch_bounds__(256) void bwd_finalize_class_kernel(const BwdFinali
     const bool k = a.shift[p] >= 0 ? ((rho ^ h) & (rp - 1)) == 0 : (rho % rp) == (h % rp);
     kept |= (uint32_t)k << p;
   }
-  if (__builtin_popcount(kept) < 2) return;
+  const bool span = (kept & a.span_mask) != 0;      // see bwd_finalize_kernel
+  if (__builtin_popcount(kept) < 2 && !span) return;
   const uint32_t t = blockIdx.x * 32 + (threadIdx.x >> 3);
   if (t >= a.rows_per_class) return;
   const int c = threadIdx.x & 7;
@@ -172,9 +177,10 @@ __global__ __launch_bounds__(256) void bwd_finalize_class_kernel(const BwdFinali
   }
 #pragma unroll
   for (int g = 0; g < 3; ++g)
-    *(uint4*)((__bf16*)a.grad[g] + out_off) =
-        uint4{pack_bf16(acc[g][0], acc[g][1]), pack_bf16(acc[g][2], acc[g][3]),
-              pack_bf16(acc[g][4], acc[g][5]), pack_bf16(acc[g][6], acc[g][7])};
+    if (g == 0 || !span)
+      *(uint4*)((__bf16*)a.grad[g] + out_off) =
+          uint4{pack_bf16(acc[g][0], acc[g][1]), pack_bf16(acc[g][2], acc[g][3]),
+                pack_bf16(acc[g][4], acc[g][5]), pack_bf16(acc[g][6], acc[g][7])};
 }
 
 hipError_t launch_bwd_finalize(const BwdFinalizeArgs& a, hipStream_t stream) {

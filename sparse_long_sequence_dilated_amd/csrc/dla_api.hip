@@ -177,6 +177,8 @@ extern "C" int dla_shard_gather(const dla_desc* desc, const dla_shape* shape,
   a.H = pl.H;
   a.r = pl.r[pattern];
   a.cr = pl.N / pl.r[pattern];
+  a.out_rows = a.cr;
+  a.out_row0 = 0;
   hipError_t e = launch_shard_gather(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "shard gather launch");
   return DLA_OK;

@@ -58,11 +58,41 @@ struct CombineArgs {
 
 // One device's part of the key/value exchange of a spanning pattern.
 struct ShardGatherArgs {
-  const void* x;           // k or v of the shard, [B, N, H, D] bf16 with strides sb/sn/sh
-  void* out;               // [B, H, cr, D] contiguous
+  const void* x;           // [B, N, H, D] bf16 with strides sb/sn/sh
+  void* out;               // [B, H, out_rows, D]; rows out_row0 .. out_row0 + cr - 1 written
   int64_t sb, sn, sh;
   int64_t B, H;
   int64_t r, cr;           // rate, cr = N / r
+  int64_t out_rows, out_row0;
+};
+
+struct ShardLdArgs {
+  const float2* ld;        // [B, H, N] (LSE * log2 e, D) pairs
+  float2* out;             // [B, H, out_rows]
+  int64_t B, H, N, r, cr, out_rows, out_row0;
+};
+
+struct ShardRelayoutArgs {
+  const void* src;
+  void* dst;
+  int64_t C, B, H, cr;     // devices of the segment, rows per device part
+  int64_t pieces;          // 16-byte pieces per row
+  int to_ext;              // [B,H,C*cr,D] -> [C,B,H,cr,D] (else the reverse)
+};
+
+struct ShardFinishArgs {
+  const float* part[kMaxP][3];   // local patterns' fp32 partial gradients [B,H,N/r,D]
+  const float* red_k[kMaxP];     // spanning patterns: exchanged dK parts [B,H,N/r,D] fp32
+  const float* red_v[kMaxP];
+  void* dk;
+  void* dv;
+  int64_t sb, sn, sh;
+  int64_t B, N, H;
+  int P;
+  int r[kMaxP];
+  int64_t nsp[kMaxP];
+  uint32_t span_mask;
+  uint32_t nblk;
 };
 
 struct RowMapArgs {
@@ -93,6 +123,12 @@ struct AttnBwdArgs {
   int64_t nsp[kMaxP];      // N / r
   Schedule sched_kv;       // dK/dV units (key tiles), all patterns
   Schedule sched_q;        // dQ units (query tiles), all patterns
+  // Query window (one sequence shard's queries in a gathered segment; single
+  // pattern, every result an fp32 partial): qhi > 0 selects it.  Query rows
+  // [qlo, qhi) exist (multiples of 128); the query schedule covers them only,
+  // and dQ partials hold nsp_q rows per (batch, head).
+  int qlo, qhi;
+  int64_t nsp_q;
 };
 
 // Sum of the per-pattern partial gradients of rows kept by several patterns.
@@ -108,6 +144,7 @@ struct BwdFinalizeArgs {
   uint32_t nblk;           // row blocks of 32 per (batch, head)
   uint32_t R;              // residue-class launch: R = lcm of the rates (0: per row)
   uint32_t rows_per_class; // N / R
+  uint32_t span_mask;      // sequence shard: patterns whose segments span devices
 };
 
 struct BwdPrepArgs {
@@ -143,6 +180,9 @@ class TimedLaunch {
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_shard_gather(const ShardGatherArgs& a, hipStream_t stream);
+hipError_t launch_shard_ld(const ShardLdArgs& a, hipStream_t stream);
+hipError_t launch_shard_relayout(const ShardRelayoutArgs& a, hipStream_t stream);
+hipError_t launch_shard_finish(const ShardFinishArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_row_map(const RowMapArgs& a, hipStream_t stream);

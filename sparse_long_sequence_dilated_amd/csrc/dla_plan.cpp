@@ -125,11 +125,18 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
   }
   p.ws_fwd = off;
 
+  p.span_mask = 0;
+  int lk_max = 0;
+  for (int i = 0; i < p.P; ++i)
+    if (p.span[i]) {
+      p.span_mask |= 1u << i;
+      lk_max = std::max(lk_max, p.Lk[i]);
+    }
   const size_t rows_all = (size_t)p.B * p.N * p.H;
   off = 0;
   p.ld_off = off;
   off = align_up(off + rows_all * 2 * sizeof(float), 256);
-  p.need_finalize = p.P > 1;
+  p.need_finalize = p.P > 1 || p.span_mask != 0;
   for (int i = 0; i < p.P; ++i)
     for (int t = 0; t < 3; ++t) {
       p.part_g_off[i][t] = (size_t)-1;
@@ -138,6 +145,16 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
       p.part_g_off[i][t] = off;
       off = align_up(off + rows * kD * sizeof(float), 256);
     }
+  for (int t = 0; t < 7; ++t) p.seg_off[t] = (size_t)-1;
+  if (p.span_mask) {
+    const size_t seg_rows = (size_t)p.B * p.H * lk_max;
+    const size_t bytes[7] = {seg_rows * kD * 2, seg_rows * kD * 2, seg_rows * 8, seg_rows * kD * 2,
+                             seg_rows * kD * 2, seg_rows * kD * 4, seg_rows * kD * 4};
+    for (int t = 0; t < 7; ++t) {
+      p.seg_off[t] = off;
+      off = align_up(off + bytes[t], 256);
+    }
+  }
   p.ws_bwd = off;
 
   // Useful (query, key) pairs; a count beyond int64 is refused.
@@ -213,12 +230,13 @@ int dla_plan_check(const dla_desc* desc, const dla_shape* shape, size_t* ws_fwd_
 }
 
 int dla_plan_check_shard(const dla_desc* desc, const dla_shape* shape, const dla_shard* shard,
-                         size_t* ws_fwd_bytes) {
+                         size_t* ws_fwd_bytes, size_t* ws_bwd_bytes) {
   if (!shard) return dla::fail(DLA_E_INVALID, "null shard");
   dla::Plan p;
   const int rc = dla::make_plan(desc, shape, &p, shard);
   if (rc != DLA_OK) return rc;
   if (ws_fwd_bytes) *ws_fwd_bytes = p.ws_fwd;
+  if (ws_bwd_bytes) *ws_bwd_bytes = p.ws_bwd;
   return DLA_OK;
 }
 

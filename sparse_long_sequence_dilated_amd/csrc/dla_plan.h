@@ -59,6 +59,12 @@ struct Plan {
   size_t part_g_off[kMaxP][3];
   bool need_finalize;           // some rows are kept by several patterns
   size_t ws_bwd;
+  // shard backward (after the partials, which persist until the finish
+  // pass): one spanning segment at a time, contiguous per (batch, head):
+  // q, dO, k, v [B,H,Lk,D] bf16, (LSE2, D) [B,H,Lk] float2, dK, dV [B,H,Lk,D]
+  // fp32, sized for the longest spanning segment.
+  uint32_t span_mask;
+  size_t seg_off[7];            // q, do, ld, k, v, dk, dv
   int64_t pairs;
 };
 

@@ -26,6 +26,7 @@ HEAD_DIM = 64
 
 EXPORTS = ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
            "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather", "dla_forward_shard",
+           "dla_backward_shard", "dla_shard_finish",
            "dla_timing_enable", "dla_timing_collect", "dla_strerror", "dla_last_error")
 
 
@@ -74,11 +75,15 @@ def lib():
     L.dla_row_map.argtypes = [pd, i64, i32, i32, vp, vp]
     L.dla_pair_count.argtypes = [pd, ps, ctypes.POINTER(i64)]
     psh = ctypes.POINTER(Shard)
-    L.dla_plan_check_shard.argtypes = [pd, ps, psh, ctypes.POINTER(sz)]
+    L.dla_plan_check_shard.argtypes = [pd, ps, psh, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     L.dla_pair_count_shard.argtypes = [pd, ps, psh, ctypes.POINTER(i64)]
     L.dla_shard_gather.argtypes = [pd, ps, psh, i32, vp, vp, vp]
     L.dla_forward_shard.argtypes = [pd, ps, psh, vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                     vp, vp, vp, sz, vp]
+    pvp = ctypes.POINTER(vp)
+    L.dla_backward_shard.argtypes = [pd, ps, psh, vp, vp, vp, vp, vp, vp, pvp, pvp, vp, vp, vp, pvp, pvp,
+                                     vp, sz, vp]
+    L.dla_shard_finish.argtypes = [pd, ps, psh, pvp, pvp, vp, vp, vp, sz, vp]
     L.dla_timing_enable.argtypes = [ctypes.c_int]
     L.dla_timing_enable.restype = ctypes.c_int
     L.dla_timing_collect.argtypes = [ctypes.c_char_p, ctypes.POINTER(i64),
@@ -90,7 +95,7 @@ def lib():
     L.dla_last_error.restype = ctypes.c_char_p
     for name in ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
                  "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather",
-                 "dla_forward_shard"):
+                 "dla_forward_shard", "dla_backward_shard", "dla_shard_finish"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -256,13 +261,14 @@ def row_map(patterns, N, H, pattern, device="cuda", stream=None):
 
 def plan_check_shard(patterns, causal, scale, B, N, H, total_rows, shard_start, D=HEAD_DIM,
                      dtype=DLA_BF16, strides=None):
-    """Forward workspace bytes of one shard; raises DlaError on an invalid shard."""
+    """(forward, backward) workspace bytes of one shard; raises DlaError on an invalid shard."""
     d = make_desc(patterns, causal, scale)
     s = make_shape(B, N, H, D, dtype, strides)
     sh = Shard(total_rows, shard_start)
-    f = ctypes.c_size_t(0)
-    _check(lib().dla_plan_check_shard(ctypes.byref(d), ctypes.byref(s), ctypes.byref(sh), ctypes.byref(f)))
-    return f.value
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().dla_plan_check_shard(ctypes.byref(d), ctypes.byref(s), ctypes.byref(sh), ctypes.byref(f),
+                                      ctypes.byref(b)))
+    return f.value, b.value
 
 
 def plan_check_shard_code(patterns, causal, scale, B, N, H, total_rows, shard_start, D=HEAD_DIM,
@@ -271,7 +277,7 @@ def plan_check_shard_code(patterns, causal, scale, B, N, H, total_rows, shard_st
     d = make_desc(patterns, causal, scale)
     s = make_shape(B, N, H, D, dtype)
     sh = Shard(total_rows, shard_start)
-    return lib().dla_plan_check_shard(ctypes.byref(d), ctypes.byref(s), ctypes.byref(sh), None)
+    return lib().dla_plan_check_shard(ctypes.byref(d), ctypes.byref(s), ctypes.byref(sh), None, None)
 
 
 def pair_count_shard(patterns, causal, B, N, H, total_rows, shard_start):
@@ -315,7 +321,7 @@ def forward_shard(q, k, v, patterns, total_rows, shard_start, ext_k=None, ext_v=
     sh = Shard(total_rows, shard_start)
     ws_f = ctypes.c_size_t(0)
     _check(lib().dla_plan_check_shard(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(sh),
-                                      ctypes.byref(ws_f)))
+                                      ctypes.byref(ws_f), None))
     B, N, H, _ = q.shape
     o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
     _same_layout(q, o)
@@ -341,3 +347,69 @@ def forward_shard(q, k, v, patterns, total_rows, shard_start, ext_k=None, ext_v=
                                    lse_t.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                    _stream(stream, q.device)))
     return o, lse_t
+
+
+def _ptr_array(P, tensors):
+    arr = (ctypes.c_void_p * P)()
+    for i, t in (tensors or {}).items():
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def backward_shard(q, k, v, o, lse, dout, patterns, total_rows, shard_start, ext_k=None, ext_v=None,
+                   causal=True, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """First half of one shard's backward.
+
+    Returns (dq, dk, dv, ext_dk, ext_dv, workspace): dq final; dk/dv final on
+    rows no spanning pattern keeps; ext_dk/ext_dv dicts {pattern: fp32
+    [w/N, B, H, N/r, D]} of this shard's contributions, to be summed over the
+    segment's devices and handed to finish_shard with the same workspace.
+    """
+    import torch
+    scale = default_scale(q.shape[-1]) if scale is None else scale
+    _same_layout(q, k, v, o, dout)
+    shape = _shape_of(q)
+    desc = make_desc(patterns, causal, scale)
+    sh = Shard(total_rows, shard_start)
+    ws_b = ctypes.c_size_t(0)
+    _check(lib().dla_plan_check_shard(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(sh), None,
+                                      ctypes.byref(ws_b)))
+    B, N, H, D = q.shape
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        _same_layout(q, g)
+        grads.append(g)
+    P = len(patterns)
+    out_k, out_v = {}, {}
+    for i, (w, r) in enumerate(patterns):
+        if w > N:
+            out_k[i] = torch.empty((w // N, B, H, N // r, D), dtype=torch.float32, device=q.device)
+            out_v[i] = torch.empty_like(out_k[i])
+    if workspace is None:
+        workspace = torch.empty(max(ws_b.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().dla_backward_shard(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(sh),
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), _ptr_array(P, ext_k), _ptr_array(P, ext_v),
+                                    grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                                    _ptr_array(P, out_k), _ptr_array(P, out_v), workspace.data_ptr(),
+                                    workspace.numel(), _stream(stream, q.device)))
+    return grads[0], grads[1], grads[2], out_k, out_v, workspace
+
+
+def finish_shard(dk, dv, patterns, total_rows, shard_start, red_dk, red_dv, workspace, causal=True,
+                 scale=None, stream=None):
+    """Second half: dk/dv of the rows spanning patterns keep, from the exchanged parts
+    red_dk/red_dv ({pattern: fp32 [B, H, N/r, D]}) and the workspace of backward_shard."""
+    scale = default_scale(dk.shape[-1]) if scale is None else scale
+    _same_layout(dk, dv)
+    shape = _shape_of(dk)
+    desc = make_desc(patterns, causal, scale)
+    sh = Shard(total_rows, shard_start)
+    P = len(patterns)
+    _check(lib().dla_shard_finish(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(sh),
+                                  _ptr_array(P, red_dk), _ptr_array(P, red_dv), dk.data_ptr(),
+                                  dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                  _stream(stream, dk.device)))
+    return dk, dv

@@ -120,3 +120,57 @@ def test_forward_shard_c4_eight_way_last_shard_sampled_rows():
         el = normwise(lse[0, h][idx].cpu().numpy(), l_ref)
         print(f"C4 shard {g}/{G} head {h}: O {eo:.3e} LSE {el:.3e}", flush=True)
         assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+BWD_CASES = [
+    # (B, total, H, patterns, causal, G): spanning patterns need N / r % 128 == 0
+    (2, 2048, 3, ((256, 1), (1024, 4), (2048, 4)), True, 4),
+    (1, 2048, 3, ((256, 1), (1024, 4), (2048, 4)), False, 4),
+    (1, 4096, 3, ((512, 1), (4096, 2)), True, 2),
+    (1, 2048, 2, ((2048, 1),), True, 4),
+    (1, 2048, 13, ((2048, 4), (1024, 2)), True, 4),               # every pattern spans
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}G{c[5]}-"
+                         f"{'c' if c[4] else 'nc'}-{'_'.join(f'{w}x{r}' for w, r in c[3])}")
+def test_backward_shards_match_whole_sequence_oracle(case):
+    """Each shard's backward, the exchange of the segments' dK/dV summed over
+    their devices (a reduce-scatter), then each shard's finish pass."""
+    import torch
+    B, total, H, pats, causal, G = case
+    N = total // G
+    seed = 7 + sum(ord(ch) for ch in str(case))
+    q, k, v, dout = inputs.random_case(seed, B, total, H, "bf16", count=4)
+    tq, tk, tv, tdo = (to_device(x, "bf16") for x in (q, k, v, dout))
+    span = [p for p, (w, r) in enumerate(pats) if w > N]
+    first = []
+    for g in range(G):
+        sl = slice(g * N, (g + 1) * N)
+        ext_k = {p: _gathered(tk, pats, p, N, total, g) for p in span}
+        ext_v = {p: _gathered(tv, pats, p, N, total, g) for p in span}
+        o, lse = dla.forward_shard(tq[:, sl], tk[:, sl], tv[:, sl], pats, total, g * N, ext_k, ext_v,
+                                   causal, 0.125)
+        first.append(dla.backward_shard(tq[:, sl], tk[:, sl], tv[:, sl], o, lse, tdo[:, sl], pats,
+                                        total, g * N, ext_k, ext_v, causal, 0.125))
+    # the exchange: device g of a segment gets the sum over the segment's devices of their parts
+    dqs, dks, dvs = [], [], []
+    for g in range(G):
+        red_k, red_v = {}, {}
+        for p in span:
+            w = pats[p][0]
+            d0 = (g * N) // w * (w // N)
+            red_k[p] = sum(first[d][3][p][g - d0] for d in range(d0, d0 + w // N)).contiguous()
+            red_v[p] = sum(first[d][4][p][g - d0] for d in range(d0, d0 + w // N)).contiguous()
+        dq, dk, dv, _, _, ws = first[g]
+        dla.finish_shard(dk, dv, pats, total, g * N, red_k, red_v, ws, causal, 0.125)
+        dqs.append(dq)
+        dks.append(dk)
+        dvs.append(dv)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, 0.125)
+    refs = oracle.backward(q, k, v, o_ref, lse_ref, dout, pats, causal, 0.125)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dqs, dks, dvs), refs):
+        e = normwise(to_host(torch.cat(got, dim=1)), ref)
+        print(f"{case} {name}: {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], (name, e)

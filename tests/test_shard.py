@@ -37,7 +37,7 @@ def test_shard_workspace_follows_closed_form():
     B, H = 2, 3
     for G in (1, 2, 4, 8):
         N = TOTAL // G
-        ws = dla.plan_check_shard(PATS, True, 0.125, B, N, H, TOTAL, (G - 1) * N)
+        ws, _ = dla.plan_check_shard(PATS, True, 0.125, B, N, H, TOTAL, (G - 1) * N)
         # partial O and LSE of every pattern but the first r == 1 one, over the shard's rows
         exp = sum(_align(B * H * (N // r) * 64 * 2) + _align(B * H * (N // r) * 4)
                   for i, (w, r) in enumerate(PATS) if i != 0)
@@ -65,7 +65,7 @@ def test_plan_check_shard_accepts_and_null_shard_is_invalid():
     assert dla.plan_check_shard_code(PATS, True, 0.125, 1, 512, 2, 2048, 1536) == dla.DLA_OK
     d = dla.make_desc(PATS, True, 0.125)
     s = dla.make_shape(1, 512, 2, 64, dla.DLA_BF16)
-    assert dla.lib().dla_plan_check_shard(d, s, None, None) == dla.DLA_E_INVALID
+    assert dla.lib().dla_plan_check_shard(d, s, None, None, None) == dla.DLA_E_INVALID
 
 
 def test_whole_sequence_as_one_shard_equals_the_plain_plan():
@@ -73,4 +73,31 @@ def test_whole_sequence_as_one_shard_equals_the_plain_plan():
         assert dla.pair_count_shard(PATS, causal, 1, TOTAL, 2, TOTAL, 0) == \
             dla.pair_count(PATS, causal, 1, TOTAL, 2)
         ws_f, _ = dla.plan_check(PATS, causal, 0.125, 1, TOTAL, 2)
-        assert dla.plan_check_shard(PATS, causal, 0.125, 1, TOTAL, 2, TOTAL, 0) == ws_f
+        assert dla.plan_check_shard(PATS, causal, 0.125, 1, TOTAL, 2, TOTAL, 0)[0] == ws_f
+
+
+def test_backward_shard_needs_128_row_parts():
+    # N / r = 64 for the spanning pattern: the forward accepts it, the backward does not
+    pats = ((256, 1), (2048, 4))
+    d = dla.make_desc(pats, True, 0.125)
+    s = dla.make_shape(1, 256, 2, 64, dla.DLA_BF16)
+    sh = dla.Shard(2048, 1792)
+    assert dla.plan_check_shard_code(pats, True, 0.125, 1, 256, 2, 2048, 1792) == dla.DLA_OK
+    L = dla.lib()
+    rc = L.dla_backward_shard(d, s, sh, *([None] * 14), 0, None)
+    assert rc == dla.DLA_E_UNSUPPORTED
+    rc = L.dla_shard_finish(d, s, sh, None, None, None, None, None, 0, None)
+    assert rc == dla.DLA_E_UNSUPPORTED
+
+
+def test_shard_backward_workspace_holds_partials_and_one_segment():
+    B, H, N = 2, 3, 512
+    _, wb = dla.plan_check_shard(PATS, True, 0.125, B, N, H, TOTAL, 0)
+    exp = _align(B * N * H * 8)
+    for w, r in PATS:
+        exp += 3 * _align(B * H * (N // r) * 64 * 4)
+    lk = max(w // r for w, r in PATS if w > N)
+    rows = B * H * lk
+    for nbytes in (rows * 128, rows * 128, rows * 8, rows * 128, rows * 128, rows * 256, rows * 256):
+        exp += _align(nbytes)
+    assert wb == exp
