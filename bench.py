@@ -12,7 +12,8 @@ Also reported, as extra fields of the same line:
   * forward-only throughput at N=32768 (B=1) and N=1,048,576 (B=1);
   * `shard_forward`: one device's share when the 1M-token sequence is split
     over 8 devices (the last shard, whose segments of the three coarsest
-    patterns span 2, 4 and 8 devices): its exchange parts and its forward;
+    patterns span 2, 4 and 8 devices): its exchange parts and its forward,
+    and (`fwd_bwd`) forward plus backward, the collectives excluded;
   * `roofline` of the kernel family that takes most of the timed region,
     timed live with HIP events around its launches on the launch stream;
   * `cpu_baseline`: the CPU oracle (float32, thread pool) on a bounded
@@ -126,7 +127,7 @@ def time_steps(step, steps, warmup):
     dla.timing_enable(False)
     fams = {}
     for fam in ("attn_fwd", "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd", "bwd_finalize",
-                "shard_gather"):
+                "shard_gather", "shard_finish"):
         n, ms = dla.timing_collect(fam)
         if n:
             fams[fam] = (n, ms)
@@ -199,7 +200,30 @@ def shard_forward(name, devices, shard, steps, warmup):
            "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS}
     for fam, (n, fms) in fams.items():
         out[f"{fam}_us_per_launch"] = 1e3 * fms / n
-    del q, k, v, o, lse, ws, ext_k, ext_v, part_k, part_v
+
+    # The backward of the same shard: its first half, then (after the
+    # exchange, not part of a one-GPU step) the finish pass.
+    dout = torch.randn_like(q)
+    red_k = {i: torch.randn((wl.B, wl.H, N // wl.patterns[i][1], wl.D), device="cuda", generator=g)
+             for i in span}
+    red_v = {i: torch.randn_like(red_k[i]) for i in span}
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    _, ws_b = dla.plan_check_shard(wl.patterns, wl.causal, wl.scale, wl.B, N, wl.H, wl.N, start)
+    wsb = torch.empty(max(ws_b, 1), dtype=torch.uint8, device="cuda")
+
+    def bstep():
+        step()
+        dla.backward_shard(q, k, v, o, lse, dout, wl.patterns, wl.N, start, ext_k, ext_v, wl.causal,
+                           wl.scale, dq=dq, dk=dk, dv=dv, workspace=wsb)
+        dla.finish_shard(dk, dv, wl.patterns, wl.N, start, red_k, red_v, wsb, wl.causal, wl.scale)
+
+    bms, bfams = time_steps(bstep, steps, warmup)
+    btf = 14 * wl.D * pairs / (bms * 1e-3) / 1e12
+    out["fwd_bwd"] = {"tokens_per_s": wl.B * N / (bms * 1e-3), "ms": bms, "useful_tflops": btf,
+                      "pct_bf16_peak": 100.0 * btf / BF16_PEAK_TFLOPS}
+    for fam, (n, fms) in bfams.items():
+        out["fwd_bwd"][f"{fam}_us_per_step"] = 1e3 * fms / steps
+    del q, k, v, o, lse, ws, ext_k, ext_v, part_k, part_v, dout, red_k, red_v, dq, dk, dv, wsb
     torch.cuda.empty_cache()
     return out
 
