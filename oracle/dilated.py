@@ -30,7 +30,10 @@ Readings where the pages are silent (each is also listed with the design
 notes): causal masking applies inside each sparsified segment by original
 position; a row no pattern selects gets output 0 and log-sum-exp -inf; the
 pattern weight is exp(LSE_p - LSE) with the unshifted denominators; duplicate
-patterns count with multiplicity; N % w == 0 and w % r == 0 are required.
+patterns count with multiplicity; w % r == 0 is required; when N is not a
+multiple of w (or w > N) the last segment holds the remaining rows only, so
+a sequence behaves as if padded to a multiple of w with rows that never
+take part (the padded rows would otherwise be keys of real queries).
 
 Layouts: q, k, v, o, dout, dq, dk, dv are [B, N, H, D]; lse is [B, H, N] in
 natural log.  Arithmetic is float64 unless `dtype` asks for float32 (the timed
@@ -45,20 +48,37 @@ import numpy as np
 
 def check_patterns(N: int, patterns) -> None:
     for w, r in patterns:
-        if not (w > 0 and r > 0 and w % r == 0 and N % w == 0):
-            raise ValueError(f"pattern (w={w}, r={r}) needs w % r == 0 and N % w == 0 (N={N})")
+        if not (w > 0 and r > 0 and w % r == 0):
+            raise ValueError(f"pattern (w={w}, r={r}) needs w % r == 0")
+
+
+def segments(N: int, w: int) -> int:
+    """Number of segments: the last one holds the N mod w remaining rows, if any."""
+    return -(-N // w)
+
+
+def segment_rows(N: int, w: int, r: int, h: int, s: int) -> np.ndarray:
+    """Original rows of segment s of pattern (w, r) for head h, in sparse order:
+    s*w + (h mod r) + a*r for every a whose row lies inside the segment and the
+    sequence ([G] 方法论: segments of length w, every r-th row, head offset
+    h mod r; a last segment shorter than w keeps the rows it has)."""
+    idx = s * w + (h % r) + r * np.arange(w // r, dtype=np.int64)
+    return idx[idx < N]
 
 
 def row_map(N: int, w: int, r: int, h: int) -> np.ndarray:
     """Original row of every sparse row of pattern (w, r) for head h.
 
     Entry s*(w/r) + a is row a of segment s after dilation: s*w + (h mod r) + a*r
-    ([G] 方法论: segments of length w, every r-th row, head offset h mod r).
+    ([G] 方法论: segments of length w, every r-th row, head offset h mod r),
+    for the first ceil(N/r) entries; an entry whose row lies past the end of
+    the sequence (in a shorter last segment) is -1.
     """
     L = w // r
-    seg = np.arange(N // w, dtype=np.int64)[:, None]
+    seg = np.arange(segments(N, w), dtype=np.int64)[:, None]
     a = np.arange(L, dtype=np.int64)[None, :]
-    return (seg * w + (h % r) + a * r).reshape(-1)
+    rows = (seg * w + (h % r) + a * r).reshape(-1)[: -(-N // r)]
+    return np.where(rows < N, rows, -1)
 
 
 def segment_attention(qs, ks, vs, scale, causal):
@@ -98,7 +118,7 @@ def combine(o_parts, lse_parts):
 
 def _units(patterns, B, H, N):
     return [(p, b, h, s) for p, (w, r) in enumerate(patterns)
-            for b in range(B) for h in range(H) for s in range(N // w)]
+            for b in range(B) for h in range(H) for s in range(segments(N, w))]
 
 
 def _run(units, fn, workers):
@@ -129,7 +149,9 @@ def forward(q, k, v, patterns, causal, scale, dtype=np.float64, workers=1):
     def unit(u):
         p, b, h, s = u
         w, r = patterns[p]
-        idx = s * w + (h % r) + r * np.arange(w // r)
+        idx = segment_rows(N, w, r, h, s)
+        if idx.size == 0:
+            return
         o, lse = segment_attention(q[b, idx, h], k[b, idx, h], v[b, idx, h], scale, causal)
         o_parts[p][b, idx, h] = o
         lse_parts[p][b, h, idx] = lse
@@ -153,7 +175,7 @@ def forward_rows(q, k, v, patterns, causal, scale, b, h, rows, dtype=np.float64)
         for w, r in patterns:
             if n % r != h % r:
                 continue
-            idx = (n // w) * w + (h % r) + r * np.arange(w // r)
+            idx = segment_rows(q.shape[1], w, r, h, n // w)
             if causal:
                 idx = idx[idx <= n]
             scores = scale * (np.asarray(k[b, idx, h], dtype) @ np.asarray(q[b, n, h], dtype))
@@ -188,11 +210,13 @@ def backward(q, k, v, o, lse, dout, patterns, causal, scale, dtype=np.float64, w
     delta = np.einsum("bnhd,bnhd->bhn", dout, o)
     dq, dk, dv = (np.zeros((B, N, H, D), dtype) for _ in range(3))
     for p, (w, r) in enumerate(patterns):
-        L = w // r
 
-        def unit(u, w=w, r=r, L=L):
+        def unit(u, w=w, r=r):
             _, b, h, s = u
-            idx = s * w + (h % r) + r * np.arange(L)
+            idx = segment_rows(N, w, r, h, s)
+            L = idx.size
+            if L == 0:
+                return
             qs, ks, vs, dos = q[b, idx, h], k[b, idx, h], v[b, idx, h], dout[b, idx, h]
             S = scale * (qs @ ks.T)
             if causal:
@@ -204,7 +228,7 @@ def backward(q, k, v, o, lse, dout, patterns, causal, scale, dtype=np.float64, w
             dq[b, idx, h] += scale * (dS @ ks)
             dk[b, idx, h] += scale * (dS.T @ qs)
 
-        units = [(p, b, h, s) for b in range(B) for h in range(H) for s in range(N // w)]
+        units = [(p, b, h, s) for b in range(B) for h in range(H) for s in range(segments(N, w))]
         _run(units, unit, workers)
     return dq, dk, dv
 
@@ -252,15 +276,18 @@ def multiplicity(N, patterns, causal, h):
 def pair_count(B, N, H, patterns, causal):
     """Unmasked (query, key) pairs the method evaluates, summed over patterns.
 
-    Per head and pattern: N/w segments of L = w/r sparse rows, each holding
-    L(L+1)/2 causal or L*L non-causal pairs.  With fixed L this grows linearly
-    in N ([G] 方法论: linear complexity O(Nd)).
+    Per head and pattern: segments of L sparse rows (L = w/r, fewer in a
+    shorter last segment), each holding L(L+1)/2 causal or L*L non-causal
+    pairs.  With fixed w/r this grows linearly in N ([G] 方法论: linear
+    complexity O(Nd)).
     """
     total = 0
     for w, r in patterns:
-        L = w // r
-        total += (N // w) * (L * (L + 1) // 2 if causal else L * L)
-    return B * H * total
+        for h in range(H):
+            for s in range(segments(N, w)):
+                L = segment_rows(N, w, r, h, s).size
+                total += L * (L + 1) // 2 if causal else L * L
+    return B * total
 
 
 def useful_flops(B, N, H, D, patterns, causal, with_backward=False):

@@ -226,8 +226,8 @@ def _torch_dense_union(q, k, v, pats, causal, scale):
     for h in range(H):
         M = torch.zeros(N, N, dtype=torch.float64)
         for w, r in pats:
-            for s in range(N // w):
-                rows = list(range(s * w + h % r, (s + 1) * w, r))
+            for s in range(-(-N // w)):                 # a last, shorter segment keeps its rows
+                rows = list(range(s * w + h % r, min((s + 1) * w, N), r))
                 for i, a in enumerate(rows):
                     for j, c in enumerate(rows):
                         if causal and j > i:
@@ -319,3 +319,85 @@ def test_row_map_properties(w, r):
         assert np.all(m // w == seg)
         kept = (np.arange(N) % r) == (h % r)
         assert np.array_equal(np.sort(m), np.nonzero(kept)[0])
+
+
+# ------------------------------------------- a shorter last segment ----
+# The pages are silent on N % w != 0; the reading taken is that the last
+# segment keeps the rows that remain (one segment of N rows when w > N).
+
+CLAMPED = [((16, 2), (64, 4)), ((12, 1), (24, 3)), ((48, 1),), ((16, 1), (32, 2), (64, 8))]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pats", CLAMPED)
+def test_clamped_forward_matches_union_softmax_brute_force(pats, causal):
+    q, k, v = _rand(hash((pats, causal, 40)) & 0xFFFF, 2, 40, 5, 8)
+    o, lse = oracle.forward(q, k, v, pats, causal, 0.3)
+    ob, lseb = oracle.brute_force_forward(q, k, v, pats, causal, 0.3)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.isfinite(lse), np.isfinite(lseb))
+    np.testing.assert_allclose(lse[np.isfinite(lse)], lseb[np.isfinite(lseb)], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_segment_longer_than_sequence_is_standard_attention(causal):
+    B, N, H, D = 1, 40, 2, 16
+    q, k, v = _rand(17, B, N, H, D)
+    o, _ = oracle.forward(q, k, v, [(64, 1)], causal, 0.25)
+    t = [torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal, scale=0.25)
+    np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("pats", CLAMPED)
+def test_causal_result_equals_padded_sequence(pats):
+    # Under the causal mask, rows appended after the sequence are never keys
+    # of a real row, so padding to a multiple of every w with arbitrary rows
+    # leaves the real rows' result unchanged.
+    N = 40
+    Np = math.lcm(*[w for w, _ in pats])
+    Np *= -(-N // Np)
+    q, k, v = _rand(61, 2, Np, 3, 8)
+    o_pad, lse_pad = oracle.forward(q, k, v, pats, True, 0.35)
+    o, lse = oracle.forward(q[:, :N], k[:, :N], v[:, :N], pats, True, 0.35)
+    np.testing.assert_allclose(o, o_pad[:, :N], rtol=1e-12, atol=1e-12)
+    fin = np.isfinite(lse)
+    assert np.array_equal(fin, np.isfinite(lse_pad[:, :, :N]))
+    np.testing.assert_allclose(lse[fin], lse_pad[:, :, :N][fin], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pats", CLAMPED[:2])
+def test_clamped_backward_matches_autograd_of_dense_union(pats, causal):
+    q, k, v, dout = _rand(71, 2, 40, 3, 8, count=4)
+    o, lse = oracle.forward(q, k, v, pats, causal, 0.4)
+    dq, dk, dv = oracle.backward(q, k, v, o, lse, dout, pats, causal, 0.4)
+    t = [torch.from_numpy(x).requires_grad_(True) for x in (q, k, v)]
+    ot = _torch_dense_union(*t, pats, causal, 0.4)
+    np.testing.assert_allclose(ot.detach().numpy(), o, rtol=1e-12, atol=1e-12)
+    ot.backward(torch.from_numpy(dout))
+    for mine, ref in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(mine, ref.grad.numpy(), rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pats", CLAMPED)
+def test_clamped_pair_count_matches_brute_force(pats, causal):
+    N, H = 40, 5
+    counted = sum(oracle.multiplicity(N, pats, causal, h).sum() for h in range(H))
+    assert oracle.pair_count(2, N, H, pats, causal) == 2 * counted
+
+
+@pytest.mark.parametrize("w,r", [(16, 2), (64, 4), (12, 3), (48, 1)])
+def test_clamped_row_map_covers_each_kept_row_once(w, r):
+    N = 40
+    for h in range(6):
+        m = oracle.row_map(N, w, r, h)
+        assert m.shape == (-(-N // r),)
+        valid = m[m >= 0]
+        assert np.array_equal(np.sort(valid), np.arange(N)[np.arange(N) % r == h % r])
+        # sparse entry s*(w/r) + a of a row in segment s
+        L = w // r
+        for i, n in enumerate(m):
+            if n >= 0:
+                assert i // L == n // w and n == (i // L) * w + h % r + (i % L) * r
