@@ -9,7 +9,10 @@
  *       1,000,000,000 Tokens", the DarcStar commentary.
  *
  * The operator ([G] 方法论, 方法详解): for each pattern (w, r) the sequence is
- * split into segments of w rows; in each segment every r-th row is kept,
+ * split into segments of w rows (the last one holds whatever rows remain
+ * when w does not divide N, all N rows when w > N; under the causal mask
+ * this equals padding the sequence to a multiple of w); in each segment
+ * every r-th row is kept,
  * starting at row (h mod r) for head h, for Q, K and V alike; dense softmax
  * attention runs inside each sparsified segment.  Patterns are merged with
  * weights exp(LSE_p - LSE), LSE = log sum_p exp(LSE_p), so the softmax
@@ -55,7 +58,7 @@ extern "C" {
 
 #define DLA_OK 0
 #define DLA_E_INVALID (-1)      /* null/misaligned pointer, bad w or r, bad scale or count */
-#define DLA_E_UNSUPPORTED (-2)  /* D != 64, N % w != 0, w % r != 0, w > N, unknown dtype */
+#define DLA_E_UNSUPPORTED (-2)  /* D != 64, w % r != 0, unknown dtype, limits exceeded */
 #define DLA_E_WORKSPACE (-3)    /* workspace smaller than dla_plan_check reports */
 #define DLA_E_HIP (-4)          /* the HIP runtime refused a launch */
 
@@ -118,10 +121,12 @@ int dla_backward(const dla_desc* desc, const dla_shape* shape, const void* q, co
 
 /*
  * Index map of one pattern ([G] 方法论: segment, dilation, head offset):
- * out[h * (N / r) + s * (w / r) + a] = s * w + (h mod r) + a * r, the original
- * row of sparse row a of segment s, for every head h < H.  out is a device
- * int32 buffer of H * (N / r) entries.  This is the address generator every
- * kernel uses, exposed so that it can be compared bit for bit.
+ * out[h * ceil(N / r) + s * (w / r) + a] = s * w + (h mod r) + a * r, the
+ * original row of sparse row a of segment s, for every head h < H, or -1
+ * when that row lies past the end of the sequence (a last segment cut
+ * short).  out is a device int32 buffer of H * ceil(N / r) entries.  This is
+ * the address generator every kernel uses, exposed so that it can be
+ * compared bit for bit.
  * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_HIP.
  */
 int dla_row_map(const dla_desc* desc, int64_t N, int32_t H, int32_t pattern, int32_t* out,
@@ -129,8 +134,9 @@ int dla_row_map(const dla_desc* desc, int64_t N, int32_t H, int32_t pattern, int
 
 /*
  * Number of (query, key) pairs the operator evaluates, summed over batch,
- * heads and patterns: B*H*sum_p (N/w_p) * (L_p(L_p+1)/2 if causal else L_p^2)
- * with L_p = w_p / r_p.  Linear in N for fixed L_p ([G] 方法论).  Host only.
+ * heads and patterns: per segment L(L+1)/2 if causal else L^2, with
+ * L = w_p / r_p (fewer in a last segment cut short, depending on the head
+ * offset).  Linear in N for fixed L ([G] 方法论).  Host only.
  * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
  */
 int dla_pair_count(const dla_desc* desc, const dla_shape* shape, int64_t* pairs);

@@ -5,8 +5,8 @@ leg may import this package.
 """
 from .dilated import (backward, brute_force_forward, check_patterns, combine, forward,
                       forward_rows, multiplicity, pair_count, row_map, segment_attention,
-                      useful_flops)
+                      segment_rows, segments, useful_flops)
 
 __all__ = ["backward", "brute_force_forward", "check_patterns", "combine", "forward",
            "forward_rows", "multiplicity", "pair_count", "row_map", "segment_attention",
-           "useful_flops"]
+           "segment_rows", "segments", "useful_flops"]

@@ -71,7 +71,9 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int li = lane & 31, lg = lane >> 5;
-  const int w = a.w[p], r = a.r[p], L = a.L[p];
+  const int w = a.w[p], r = a.r[p], L_full = a.L[p];
+  const int L = seg_rows(a.N, seg, w, r, h, L_full);  // fewer in a cut-short last segment
+  if (tile * kBwdRows >= L) return;                    // nothing of this segment left
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const int64_t rstride = (int64_t)r * a.sn;
@@ -442,7 +444,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     // (a window's dQ partial holds the window's rows only: nsp_q rows per
     // (batch, head), its base shifted back by qlo rows by the caller)
     const int64_t nsp = (kWin && !kKV) ? a.nsp_q : a.nsp[p];
-    const int64_t part_row0 = ((int64_t)b * a.H + h) * nsp + seg * L + own0;
+    const int64_t part_row0 = ((int64_t)b * a.H + h) * nsp + seg * L_full + own0;
 #pragma unroll 2
     for (int it = 0; it < 8; ++it) {
       const int rr = 4 * it + (lane >> 4);

@@ -71,13 +71,17 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // L query rows (local), Lk key rows; local query row i is row qoff + i of
   // the segment (qoff = 0 and Lk = L except for a segment that spans
   // several sequence shards, whose keys come from the gathered buffers).
-  const int w = a.w[p], r = a.r[p], L = a.L[p];
+  const int w = a.w[p], r = a.r[p], L_full = a.L[p];
+  // A cut-short last segment holds fewer rows (a pattern spanning shards
+  // never has one: its segment is whole by construction).
+  const bool ext = kShard && a.ext_k[p] != nullptr;
+  const int L = ext ? L_full : seg_rows(a.N, seg, w, r, h, L_full);
+  if (tile * kFwdBM >= L) return;                      // nothing of this segment left
   const int Lk = kShard ? a.Lk[p] : L, qoff = kShard ? a.qoff[p] : 0;
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const int64_t rstride = (int64_t)r * a.sn;  // elements between consecutive sparse rows
   const __bf16* Qh = (const __bf16*)a.q + head_off + base_row * a.sn;
-  const bool ext = kShard && a.ext_k[p] != nullptr;
   const int64_t cr = a.nsp[p];                 // rows per gathered chunk
   const __bf16* Kh = ext ? (const __bf16*)a.ext_k[p] + ((int64_t)b * a.H + h) * cr * kD
                          : (const __bf16*)a.k + head_off + base_row * a.sn;
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
     dst = (__bf16*)a.o + head_off + n * a.sn;
     lse_dst = a.lse + bh * a.N + n;
   } else {
-    const int64_t m = seg * L + row;
+    const int64_t m = seg * L_full + row;
     dst = (__bf16*)a.part_o[p] + (bh * nsparse + m) * kD;
     lse_dst = a.part_lse[p] + bh * nsparse + m;
   }

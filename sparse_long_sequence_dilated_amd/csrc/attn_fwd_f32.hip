@@ -20,7 +20,9 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const AttnFwdArgs a) 
   int p, b, h, tile;
   int64_t seg;
   decode_unit(a.sched, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile);
-  const int w = a.w[p], r = a.r[p], L = a.L[p];
+  const int w = a.w[p], r = a.r[p], L_full = a.L[p];
+  const int L = seg_rows(a.N, seg, w, r, h, L_full);  // fewer in a cut-short last segment
+  if (tile * kF32BM >= L) return;                      // nothing of this segment left
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const int64_t rstride = (int64_t)r * a.sn;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const AttnFwdArgs a) 
     lse_dst = a.lse + bh * a.N + n;
   } else {
     const int64_t nsparse = a.nsp[p];
-    const int64_t m = seg * L + row;
+    const int64_t m = seg * L_full + row;
     dst = (float*)a.part_o[p] + (bh * nsparse + m) * kD;
     lse_dst = a.part_lse[p] + bh * nsparse + m;
   }

@@ -252,20 +252,22 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream) {
 }
 
 // Integer index map of one pattern, exposed so the address generator can be
-// compared bit for bit: out[h*(N/r) + m] = original row of sparse row m.
+// compared bit for bit: out[h*ceil(N/r) + m] = original row of sparse row m,
+// or -1 past the end of a cut-short last segment.
 __global__ __launch_bounds__(256) void row_map_kernel(const RowMapArgs a) {
-  const int64_t per_head = a.N / a.r;
+  const int64_t per_head = (a.N + a.r - 1) / a.r;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= per_head * a.H) return;
   const int h = (int)(gid / per_head);
   const int64_t m = gid - (int64_t)h * per_head;
   const int64_t seg = m / a.L;
   const int64_t row = m - seg * a.L;
-  a.out[gid] = (int32_t)(seg_base_row(seg, a.w, a.r, h) + row * a.r);
+  const int64_t n = seg_base_row(seg, a.w, a.r, h) + row * a.r;
+  a.out[gid] = n < a.N ? (int32_t)n : -1;                // past the end of a cut-short segment
 }
 
 hipError_t launch_row_map(const RowMapArgs& a, hipStream_t stream) {
-  const int64_t n = (a.N / a.r) * a.H;
+  const int64_t n = ((a.N + a.r - 1) / a.r) * a.H;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(row_map_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();

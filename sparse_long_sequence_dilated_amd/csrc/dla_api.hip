@@ -36,7 +36,7 @@ static void fill_fwd_args(const Plan& pl, AttnFwdArgs* a) {
     a->r[i] = pl.r[i];
     a->L[i] = pl.L[i];
     a->nseg[i] = pl.nseg[i];
-    a->nsp[i] = pl.N / pl.r[i];
+    a->nsp[i] = pl.nsp[i];
     a->Lk[i] = pl.Lk[i];
     a->qoff[i] = pl.qoff[i];
   }
@@ -88,7 +88,7 @@ static int forward_impl(const Plan& pl, const void* q, const void* k, const void
       cb.part_o[i] = a.part_o[i];
       cb.part_lse[i] = a.part_lse[i];
       cb.r[i] = pl.r[i];
-      cb.nsp[i] = pl.N / pl.r[i];
+      cb.nsp[i] = pl.nsp[i];
     }
     cb.sb = pl.sb;
     cb.sn = pl.sn;
@@ -106,7 +106,7 @@ static int forward_impl(const Plan& pl, const void* q, const void* k, const void
     if (nblk * pl.B > 0x7FFFFFFF)
       return fail(DLA_E_UNSUPPORTED, "B * N / 32 exceeds the launch grid");
     cb.nblk = (uint32_t)nblk;
-    // R = lcm of the rates divides N (every r divides its w, which divides N).
+    // R = lcm of the rates; the residue-class launch needs R | N.
     int64_t R = 1;
     for (int i = 0; i < pl.P; ++i) {
       int64_t g = R, x = pl.r[i];

@@ -28,9 +28,8 @@ static int hip_fail(hipError_t e, const char* what) {
   return fail(DLA_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// lcm of the rates when the residue-class launch fits (rows per class >= 32),
-// else 0.  R divides N: every r divides its w, which divides N (or, for a
-// pattern spanning shards, divides N directly).
+// lcm of the rates when the residue-class launch fits (R divides N and rows
+// per class >= 32), else 0 (the per-row launch).
 static void residue_classes(const Plan& pl, uint32_t* R_out, uint32_t* rpc_out) {
   int64_t R = 1;
   for (int i = 0; i < pl.P; ++i) {
@@ -101,7 +100,7 @@ static int run_attention(const Plan& pl, const void* q, const void* k, const voi
     a.r[i] = pl.r[i];
     a.L[i] = pl.L[i];
     a.nseg[i] = pl.nseg[i];
-    a.nsp[i] = pl.N / pl.r[i];
+    a.nsp[i] = pl.nsp[i];
     for (int g = 0; g < 3; ++g)
       a.part[i][g] = pl.need_finalize ? (float*)(wsb + pl.part_g_off[i][g]) : nullptr;
     if (pl.span[i]) local.nseg[i] = 0;
@@ -120,7 +119,7 @@ static int run_finalize(const Plan& pl, char* wsb, void* dq, void* dk, void* dv,
   for (int i = 0; i < pl.P; ++i) {
     for (int g = 0; g < 3; ++g) f.part[i][g] = (const float*)(wsb + pl.part_g_off[i][g]);
     f.r[i] = pl.r[i];
-    f.nsp[i] = pl.N / pl.r[i];
+    f.nsp[i] = pl.nsp[i];
     f.shift[i] = (pl.r[i] & (pl.r[i] - 1)) == 0 ? __builtin_ctz((unsigned)pl.r[i]) : -1;
   }
   f.grad[0] = dq;
@@ -358,7 +357,7 @@ extern "C" int dla_shard_finish(const dla_desc* desc, const dla_shape* shape,
       f.red_v[i] = red_dv[i];
     }
     f.r[i] = pl.r[i];
-    f.nsp[i] = pl.N / pl.r[i];
+    f.nsp[i] = pl.nsp[i];
   }
   f.dk = dk;
   f.dv = dv;

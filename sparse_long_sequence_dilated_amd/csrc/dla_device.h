@@ -25,6 +25,16 @@ __device__ __forceinline__ int64_t seg_base_row(int64_t seg, int w, int r, int h
   return seg * (int64_t)w + (h % r);
 }
 
+// Sparse rows of segment seg for head h: L_full = w/r, or fewer in a last
+// segment that the end of the sequence cuts short (rows (h mod r) + a*r
+// below the N - seg*w rows that remain).
+__device__ __forceinline__ int seg_rows(int64_t N, int64_t seg, int w, int r, int h, int L_full) {
+  const int64_t left = N - seg * (int64_t)w;
+  if (left >= w) return L_full;
+  const int off = h % r;
+  return left > off ? (int)((left - 1 - off) / r) + 1 : 0;
+}
+
 // Longest-first unit decode (see Schedule in dla_plan.h).  All quantities fit
 // in 32 bits (the planner bounds the unit count by the launch grid), so the
 // divisions are 32-bit.

@@ -81,12 +81,16 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
     const int w = desc->patterns[i].w, r = desc->patterns[i].r;
     if (w < 1 || r < 1) return fail(DLA_E_INVALID, "pattern %d: w=%d r=%d must be >= 1", i, w, r);
     if (w % r) return fail(DLA_E_UNSUPPORTED, "pattern %d: r=%d does not divide w=%d", i, r, w);
-    if (w > total) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d exceeds N=%lld", i, w,
-                               (long long)total);
-    if (total % w) return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d does not divide N=%lld", i, w,
-                               (long long)total);
-    const bool spans = w > p.N;  // only with a shard: w <= total
-    if (!spans && p.N % w)
+    // A whole sequence may end inside a segment (its last segment is cut
+    // short); a sequence split over shards needs whole segments.
+    if (shard && w > total)
+      return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d exceeds the sequence of %lld rows", i, w,
+                  (long long)total);
+    if (shard && total % w)
+      return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d does not divide the sequence of %lld rows",
+                  i, w, (long long)total);
+    const bool spans = shard && w > p.N;
+    if (shard && !spans && p.N % w)
       return fail(DLA_E_UNSUPPORTED, "pattern %d: w=%d does not divide the shard length N=%lld", i,
                   w, (long long)p.N);
     if (spans && (w % p.N || p.N % r || (p.N / r) % 64))
@@ -103,7 +107,8 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
     p.Lk[i] = w / r;
     p.L[i] = spans ? (int)(p.N / r) : w / r;
     p.qoff[i] = spans ? (int)((start % w) / r) : 0;
-    p.nseg[i] = spans ? 1 : p.N / w;
+    p.nseg[i] = spans ? 1 : (p.N + w - 1) / w;
+    p.nsp[i] = (p.N + r - 1) / r;
   }
 
   // The pattern that keeps the most rows (smallest r, first on ties) writes
@@ -117,7 +122,7 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
   for (int i = 0; i < p.P; ++i) {
     p.part_o_off[i] = p.part_lse_off[i] = (size_t)-1;
     if (i == p.prim) continue;
-    const size_t rows = (size_t)p.B * p.H * (p.N / p.r[i]);
+    const size_t rows = (size_t)p.B * p.H * p.nsp[i];
     p.part_o_off[i] = off;
     off = align_up(off + rows * kD * p.esize, 256);
     p.part_lse_off[i] = off;
@@ -141,7 +146,7 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
     for (int t = 0; t < 3; ++t) {
       p.part_g_off[i][t] = (size_t)-1;
       if (!p.need_finalize) continue;
-      const size_t rows = (size_t)p.B * p.H * (p.N / p.r[i]);
+      const size_t rows = (size_t)p.B * p.H * p.nsp[i];
       p.part_g_off[i][t] = off;
       off = align_up(off + rows * kD * sizeof(float), 256);
     }
@@ -177,11 +182,21 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
       ovf |= __builtin_mul_overflow(L, p.causal ? L + 1 : L, &per);
       if (p.causal) per /= 2;
     }
-    ovf |= __builtin_mul_overflow(p.nseg[i], per, &seg_pairs);
+    // per (batch, head): whole segments, then a cut-short last one whose
+    // row count depends on the head offset
+    const int64_t whole = p.span[i] ? 1 : p.N / p.w[i];
+    ovf |= __builtin_mul_overflow(whole, per, &seg_pairs);
+    ovf |= __builtin_mul_overflow(seg_pairs, p.H, &seg_pairs);
+    const int64_t left = p.N - whole * p.w[i];
+    if (!p.span[i] && left > 0)
+      for (int64_t h = 0; h < p.H; ++h) {
+        const int64_t off = h % p.r[i];
+        const int64_t Ls = left > off ? (left - 1 - off) / p.r[i] + 1 : 0;
+        ovf |= __builtin_add_overflow(seg_pairs, p.causal ? Ls * (Ls + 1) / 2 : Ls * Ls, &seg_pairs);
+      }
     ovf |= __builtin_add_overflow(pairs, seg_pairs, &pairs);
   }
   ovf |= __builtin_mul_overflow(pairs, p.B, &pairs);
-  ovf |= __builtin_mul_overflow(pairs, p.H, &pairs);
   if (ovf) return fail(DLA_E_UNSUPPORTED, "the number of attention pairs exceeds 2^63");
   p.pairs = pairs;
   return DLA_OK;

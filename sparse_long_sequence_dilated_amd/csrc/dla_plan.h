@@ -37,7 +37,8 @@ struct Plan {
   int causal;
   float scale;
   int w[kMaxP], r[kMaxP], L[kMaxP];
-  int64_t nseg[kMaxP];
+  int64_t nseg[kMaxP];          // ceil(N / w): a last segment may be cut short
+  int64_t nsp[kMaxP];           // ceil(N / r): sparse rows per (batch, head)
   // Sequence shard (dla_forward_shard): a pattern whose segments are longer
   // than the shard spans devices; the shard holds L = N/r of its Lk = w/r
   // sparse rows, starting at sparse row qoff of one segment (nseg = 1).

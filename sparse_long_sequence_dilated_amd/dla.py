@@ -251,7 +251,7 @@ def row_map(patterns, N, H, pattern, device="cuda", stream=None):
     import torch
     desc = make_desc(patterns, False, 1.0)
     r = patterns[pattern][1]
-    out = torch.empty((H, N // r), dtype=torch.int32, device=device)
+    out = torch.empty((H, -(-N // r)), dtype=torch.int32, device=device)
     _check(lib().dla_row_map(ctypes.byref(desc), N, H, pattern, out.data_ptr(),
                              _stream(stream, out.device)))
     return out

@@ -53,8 +53,6 @@ C3 = inputs.WORKLOADS["C3"]
     (dict(patterns=[(64, 0)]), dla.DLA_E_INVALID),
     (dict(patterns=[(64, -2)]), dla.DLA_E_INVALID),
     (dict(patterns=[(64, 3)]), dla.DLA_E_UNSUPPORTED),       # r does not divide w
-    (dict(patterns=[(96, 1)]), dla.DLA_E_UNSUPPORTED),       # w does not divide N
-    (dict(patterns=[(512, 1)]), dla.DLA_E_UNSUPPORTED),      # w > N
     (dict(scale=float("nan")), dla.DLA_E_INVALID),
     (dict(scale=float("inf")), dla.DLA_E_INVALID),
     (dict(scale=0.0), dla.DLA_E_INVALID),
@@ -81,6 +79,29 @@ def test_plan_check_rejects(kwargs, code):
         rc = dla.plan_check_code(args.pop("patterns"), causal, args.pop("scale"), **args)
     assert rc == code
     assert dla.lib().dla_last_error()
+
+
+def test_segments_cut_short_are_valid():
+    # w that does not divide N, and w > N: the last segment keeps the rows that remain
+    for pats in ([(96, 1)], [(512, 1)], [(96, 1), (512, 4)], [(100, 4)]):
+        assert dla.plan_check_code(pats, True, 0.125, 1, 256, 2) == dla.DLA_OK
+
+
+@pytest.mark.parametrize("pats", [((96, 1),), ((512, 1),), ((96, 1), (512, 4)), ((100, 4), (48, 3)),
+                                  ((3000, 2),)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_pair_count_cut_short_segments_matches_oracle(pats, causal):
+    for N in (256, 1000, 2049):
+        assert dla.pair_count(pats, causal, 2, N, 7) == oracle.pair_count(2, N, 7, pats, causal)
+
+
+def test_workspace_cut_short_segments_uses_ceil_rows():
+    # N / r rounded up: the sparse index of row n stays n // r
+    N, B, H = 1000, 2, 3
+    ws_f, ws_b = dla.plan_check([(96, 1), (510, 3)], True, 0.125, B, N, H)
+    rows = B * H * (-(-N // 3))
+    assert ws_f == _align(rows * 64 * 2) + _align(rows * 4)
+    assert ws_b == _align(B * N * H * 8) + 3 * _align(B * H * N * 64 * 4) + 3 * _align(rows * 64 * 4)
 
 
 def test_empty_batch_and_heads_are_valid():
@@ -151,7 +172,7 @@ int main(void) {
   d.num_patterns = 17; bad += expect(dla_plan_check(&d, &s, NULL, NULL), DLA_E_INVALID, "17 patterns");
   d.num_patterns = 5; d.patterns = NULL; bad += expect(dla_plan_check(&d, &s, NULL, NULL), DLA_E_INVALID, "null patterns");
   d.patterns = pats; d.scale = NAN; bad += expect(dla_plan_check(&d, &s, NULL, NULL), DLA_E_INVALID, "nan");
-  d.scale = 0.125f; s.N = 32768 + 64; bad += expect(dla_plan_check(&d, &s, NULL, NULL), DLA_E_UNSUPPORTED, "N%w");
+  d.scale = 0.125f; s.N = 32768 + 64; bad += expect(dla_plan_check(&d, &s, NULL, NULL), DLA_OK, "last segment cut short");
   s.N = 32768; s.D = 32; bad += expect(dla_plan_check(&d, &s, NULL, NULL), DLA_E_UNSUPPORTED, "D");
   s.D = 64; s.dtype = 5; bad += expect(dla_plan_check(&d, &s, NULL, NULL), DLA_E_UNSUPPORTED, "dtype");
   s.dtype = DLA_F32; s.stride_h = 4; bad += expect(dla_plan_check(&d, &s, NULL, NULL), DLA_E_INVALID, "stride");

@@ -29,6 +29,11 @@ SMALL = [
     # N / lcm(r) < 32: the finalize pass runs per row instead of per residue class
     (1, 256, 3, ((256, 1), (128, 16)), True, "bnhd"),
     (2, 512, 2, ((512, 1), (256, 32), (512, 2)), False, "bnhd"),
+    # a last segment cut short (w does not divide N, or w > N)
+    (2, 1000, 3, ((256, 1), (512, 2), (2048, 4)), True, "bnhd"),
+    (1, 1000, 3, ((256, 1), (512, 2), (2048, 4)), False, "bnhd"),
+    (1, 602, 5, ((300, 4), (640, 1)), True, "bhnd"),               # heads 2, 3: last segment empty
+    (1, 1000, 2, ((4096, 1),), True, "bnhd"),
 ]
 
 

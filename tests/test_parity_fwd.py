@@ -38,6 +38,13 @@ SMALL = [
     # N / lcm(r) < 32: the merge runs per row instead of per residue class
     (1, 256, 3, ((256, 1), (128, 16)), True, "bf16", "bnhd"),
     (2, 512, 2, ((512, 1), (256, 32)), False, "f32", "bnhd"),
+    # a last segment cut short (w does not divide N, or w > N)
+    (2, 1000, 3, ((256, 1), (512, 2), (2048, 4)), True, "bf16", "bnhd"),
+    (1, 1000, 3, ((256, 1), (512, 2), (2048, 4)), False, "bf16", "bnhd"),
+    (1, 602, 5, ((300, 4), (640, 1)), True, "bf16", "bhnd"),        # heads 2, 3: last segment empty
+    (1, 1000, 2, ((4096, 1),), True, "bf16", "bnhd"),                # one segment shorter than w
+    (2, 500, 3, ((128, 1), (256, 2), (1024, 4)), True, "f32", "bnhd"),
+    (1, 500, 3, ((200, 4), (1024, 1)), False, "f32", "bnhd"),
 ]
 
 
@@ -78,6 +85,14 @@ def test_forward_rejects_bad_workspace():
         dla.forward(q, q, q, [(64, 1), (256, 4)], True,
                     workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert ei.value.code == dla.DLA_E_WORKSPACE
+
+
+@pytest.mark.parametrize("N,pats", [(1000, ((256, 1), (512, 2), (2048, 4))), (602, ((300, 4), (640, 1)))])
+def test_row_map_cut_short_segments_bit_exact(N, pats):
+    for p, (w, r) in enumerate(pats):
+        got = dla.row_map(pats, N, 5, p).cpu().numpy()
+        for h in range(5):
+            assert np.array_equal(got[h], oracle.row_map(N, w, r, h)), (N, p, h)
 
 
 @pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4"])
