@@ -34,6 +34,9 @@ patterns count with multiplicity; w % r == 0 is required; when N is not a
 multiple of w (or w > N) the last segment holds the remaining rows only, so
 a sequence behaves as if padded to a multiple of w with rows that never
 take part (the padded rows would otherwise be keys of real queries).
+Batches of different lengths (`lengths`): batch b is the sequence of its
+first lengths[b] rows; the rows after it are padding and get output 0,
+log-sum-exp -inf and zero gradients.
 
 Layouts: q, k, v, o, dout, dq, dk, dv are [B, N, H, D]; lse is [B, H, N] in
 natural log.  Arithmetic is float64 unless `dtype` asks for float32 (the timed
@@ -132,24 +135,30 @@ def _run(units, fn, workers):
             pass
 
 
-def forward(q, k, v, patterns, causal, scale, dtype=np.float64, workers=1):
+def _lengths(lengths, B, N):
+    return [N] * B if lengths is None else [int(x) for x in lengths]
+
+
+def forward(q, k, v, patterns, causal, scale, dtype=np.float64, workers=1, lengths=None):
     """Dilated attention forward; returns (O [B,N,H,D], LSE [B,H,N]).
 
     An explicit loop over pattern, batch, head and segment: gather the rows the
     pattern keeps, attend densely inside the segment, scatter the result back
     into a per-pattern buffer (rows a pattern does not select keep O_p = 0,
-    LSE_p = -inf), then merge the patterns with `combine`.
+    LSE_p = -inf), then merge the patterns with `combine`.  With `lengths`,
+    batch b's sequence is its first lengths[b] rows.
     """
     q, k, v = (np.asarray(t, dtype=dtype) for t in (q, k, v))
     B, N, H, D = q.shape
     check_patterns(N, patterns)
+    lens = _lengths(lengths, B, N)
     o_parts = [np.zeros((B, N, H, D), dtype) for _ in patterns]
     lse_parts = [np.full((B, H, N), -np.inf, dtype) for _ in patterns]
 
     def unit(u):
         p, b, h, s = u
         w, r = patterns[p]
-        idx = segment_rows(N, w, r, h, s)
+        idx = segment_rows(lens[b], w, r, h, s)
         if idx.size == 0:
             return
         o, lse = segment_attention(q[b, idx, h], k[b, idx, h], v[b, idx, h], scale, causal)
@@ -193,7 +202,8 @@ def forward_rows(q, k, v, patterns, causal, scale, b, h, rows, dtype=np.float64)
     return np.array(out_o, dtype), np.array(out_lse, dtype)
 
 
-def backward(q, k, v, o, lse, dout, patterns, causal, scale, dtype=np.float64, workers=1):
+def backward(q, k, v, o, lse, dout, patterns, causal, scale, dtype=np.float64, workers=1,
+             lengths=None):
     """Analytic gradients (dQ, dK, dV) of the combined forward w.r.t. q, k, v.
 
     The combined output is one softmax over the union (with multiplicity) of
@@ -207,13 +217,14 @@ def backward(q, k, v, o, lse, dout, patterns, causal, scale, dtype=np.float64, w
     lse = np.asarray(lse, dtype=dtype)
     B, N, H, D = q.shape
     check_patterns(N, patterns)
+    lens = _lengths(lengths, B, N)
     delta = np.einsum("bnhd,bnhd->bhn", dout, o)
     dq, dk, dv = (np.zeros((B, N, H, D), dtype) for _ in range(3))
     for p, (w, r) in enumerate(patterns):
 
         def unit(u, w=w, r=r):
             _, b, h, s = u
-            idx = segment_rows(N, w, r, h, s)
+            idx = segment_rows(lens[b], w, r, h, s)
             L = idx.size
             if L == 0:
                 return
@@ -233,7 +244,7 @@ def backward(q, k, v, o, lse, dout, patterns, causal, scale, dtype=np.float64, w
     return dq, dk, dv
 
 
-def brute_force_forward(q, k, v, patterns, causal, scale):
+def brute_force_forward(q, k, v, patterns, causal, scale, lengths=None):
     """Union-softmax form on a dense N x N matrix; for tiny inputs only.
 
     M_h[q, k] counts the patterns whose dilated segment holds both q and k:
@@ -243,11 +254,16 @@ def brute_force_forward(q, k, v, patterns, causal, scale):
     """
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     B, N, H, D = q.shape
+    lens = _lengths(lengths, B, N)
     o = np.zeros((B, N, H, D))
     lse = np.full((B, H, N), -np.inf)
     for h in range(H):
-        M = multiplicity(N, patterns, causal, h)
         for b in range(B):
+            # a row at or past the batch's length is in no segment
+            n = np.arange(N)
+            real = n < lens[b]
+            M = multiplicity(lens[b], patterns, causal, h) if lens[b] > 0 else np.zeros((0, 0))
+            M = np.pad(M, ((0, N - lens[b]), (0, N - lens[b]))) * (real[:, None] & real[None, :])
             S = scale * (q[b, :, h] @ k[b, :, h].T)
             covered = M.sum(axis=1) > 0
             m = np.where(M > 0, S, -np.inf).max(axis=1)
@@ -273,7 +289,7 @@ def multiplicity(N, patterns, causal, h):
     return M
 
 
-def pair_count(B, N, H, patterns, causal):
+def pair_count(B, N, H, patterns, causal, lengths=None):
     """Unmasked (query, key) pairs the method evaluates, summed over patterns.
 
     Per head and pattern: segments of L sparse rows (L = w/r, fewer in a
@@ -282,12 +298,13 @@ def pair_count(B, N, H, patterns, causal):
     complexity O(Nd)).
     """
     total = 0
-    for w, r in patterns:
-        for h in range(H):
-            for s in range(segments(N, w)):
-                L = segment_rows(N, w, r, h, s).size
-                total += L * (L + 1) // 2 if causal else L * L
-    return B * total
+    for n_b in _lengths(lengths, B, N):
+        for w, r in patterns:
+            for h in range(H):
+                for s in range(segments(n_b, w)):
+                    L = segment_rows(n_b, w, r, h, s).size
+                    total += L * (L + 1) // 2 if causal else L * L
+    return total
 
 
 def useful_flops(B, N, H, D, patterns, causal, with_backward=False):

@@ -401,3 +401,51 @@ def test_clamped_row_map_covers_each_kept_row_once(w, r):
         for i, n in enumerate(m):
             if n >= 0:
                 assert i // L == n // w and n == (i // L) * w + h % r + (i % L) * r
+
+
+# ---------------------------------------------- batches of different lengths ----
+# Batch b is the sequence of its first lengths[b] rows; the rows after it are
+# padding (output 0, log-sum-exp -inf, zero gradients).
+
+VARLEN = [(40, 17, 0, 33), (40, 40, 1, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pats", [((16, 2), (64, 4)), ((12, 1), (24, 3))])
+@pytest.mark.parametrize("lens", VARLEN)
+def test_varlen_forward_matches_union_softmax_brute_force(pats, causal, lens):
+    N = max(max(lens), 40)
+    q, k, v = _rand(hash((pats, causal, lens)) & 0xFFFF, len(lens), N, 3, 8)
+    o, lse = oracle.forward(q, k, v, pats, causal, 0.3, lengths=lens)
+    ob, lseb = oracle.brute_force_forward(q, k, v, pats, causal, 0.3, lengths=lens)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.isfinite(lse), np.isfinite(lseb))
+    np.testing.assert_allclose(lse[np.isfinite(lse)], lseb[np.isfinite(lseb)], rtol=1e-12, atol=1e-12)
+    for b, n_b in enumerate(lens):
+        assert np.all(o[b, n_b:] == 0.0) and np.all(lse[b, :, n_b:] == -np.inf)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_backward_matches_autograd_of_dense_union(causal):
+    pats = [(16, 2), (64, 4)]
+    lens = (40, 23)
+    q, k, v, dout = _rand(81, 2, 40, 3, 8, count=4)
+    o, lse = oracle.forward(q, k, v, pats, causal, 0.4, lengths=lens)
+    dq, dk, dv = oracle.backward(q, k, v, o, lse, dout, pats, causal, 0.4, lengths=lens)
+    for b, n_b in enumerate(lens):
+        t = [torch.from_numpy(x[b:b + 1, :n_b].copy()).requires_grad_(True) for x in (q, k, v)]
+        ot = _torch_dense_union(*t, pats, causal, 0.4)
+        np.testing.assert_allclose(ot.detach().numpy()[0], o[b, :n_b], rtol=1e-12, atol=1e-12)
+        ot.backward(torch.from_numpy(dout[b:b + 1, :n_b].copy()))
+        for mine, ref in zip((dq, dk, dv), t):
+            np.testing.assert_allclose(mine[b, :n_b], ref.grad.numpy()[0], rtol=1e-11, atol=1e-11)
+            assert np.all(mine[b, n_b:] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_pair_count_matches_brute_force(causal):
+    pats = ((16, 2), (64, 4), (12, 1))
+    lens = (40, 17, 0, 33)
+    want = sum(oracle.multiplicity(n_b, pats, causal, h).sum() for n_b in lens if n_b
+               for h in range(5))
+    assert oracle.pair_count(len(lens), 40, 5, pats, causal, lengths=lens) == want
