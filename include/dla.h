@@ -120,6 +120,35 @@ int dla_backward(const dla_desc* desc, const dla_shape* shape, const void* q, co
                  void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---- Batches of different lengths ----
+ *
+ * The same operator on a padded batch: batch b's sequence is its first
+ * lengths[b] rows (segments are cut at that length as at the end of any
+ * sequence); the rows after it are padding, with o = 0, lse = -inf and zero
+ * gradients, and take no part in any other row's attention.  lengths is a
+ * device int32 buffer of B entries, read by the kernels; an entry outside
+ * [0, N] is clamped to that range.  The workspace sizes are those of
+ * dla_plan_check for the padded shape.
+ * Errors: as dla_forward / dla_backward, and DLA_E_INVALID for a null or
+ * misaligned lengths pointer (B > 0 and H > 0).
+ */
+int dla_forward_varlen(const dla_desc* desc, const dla_shape* shape, const int32_t* lengths,
+                       const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* ws, size_t ws_bytes, void* stream);
+int dla_backward_varlen(const dla_desc* desc, const dla_shape* shape, const int32_t* lengths,
+                        const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dla_pair_count for batches of different lengths; here lengths is host
+ * memory (B entries, clamped to [0, N]).  Host only.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.
+ */
+int dla_pair_count_varlen(const dla_desc* desc, const dla_shape* shape, const int32_t* lengths,
+                          int64_t* pairs);
+
+/*
  * Index map of one pattern ([G] 方法论: segment, dilation, head offset):
  * out[h * ceil(N / r) + s * (w / r) + a] = s * w + (h mod r) + a * r, the
  * original row of sparse row a of segment s, for every head h < H, or -1

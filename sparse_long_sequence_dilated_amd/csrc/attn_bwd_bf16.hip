@@ -72,7 +72,8 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int li = lane & 31, lg = lane >> 5;
   const int w = a.w[p], r = a.r[p], L_full = a.L[p];
-  const int L = seg_rows(a.N, seg, w, r, h, L_full);  // fewer in a cut-short last segment
+  // fewer in a cut-short last segment (of the sequence or of this batch's)
+  const int L = seg_rows(batch_len(a.lengths, b, a.N), seg, w, r, h, L_full);
   if (tile * kBwdRows >= L) return;                    // nothing of this segment left
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;

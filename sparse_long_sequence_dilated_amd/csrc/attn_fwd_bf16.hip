@@ -75,7 +75,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // A cut-short last segment holds fewer rows (a pattern spanning shards
   // never has one: its segment is whole by construction).
   const bool ext = kShard && a.ext_k[p] != nullptr;
-  const int L = ext ? L_full : seg_rows(a.N, seg, w, r, h, L_full);
+  const int L = ext ? L_full : seg_rows(batch_len(a.lengths, b, a.N), seg, w, r, h, L_full);
   if (tile * kFwdBM >= L) return;                      // nothing of this segment left
   const int Lk = kShard ? a.Lk[p] : L, qoff = kShard ? a.qoff[p] : 0;
   const int64_t base_row = seg_base_row(seg, w, r, h);

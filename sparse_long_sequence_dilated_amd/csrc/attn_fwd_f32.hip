@@ -21,7 +21,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const AttnFwdArgs a) 
   int64_t seg;
   decode_unit(a.sched, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile);
   const int w = a.w[p], r = a.r[p], L_full = a.L[p];
-  const int L = seg_rows(a.N, seg, w, r, h, L_full);  // fewer in a cut-short last segment
+  // fewer in a cut-short last segment (of the sequence or of this batch's)
+  const int L = seg_rows(batch_len(a.lengths, b, a.N), seg, w, r, h, L_full);
   if (tile * kF32BM >= L) return;                      // nothing of this segment left
   const int64_t base_row = seg_base_row(seg, w, r, h);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;

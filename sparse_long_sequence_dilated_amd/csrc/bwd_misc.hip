@@ -59,10 +59,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdPrepArgs a) {
     const int64_t i = (b * a.H + h) * a.N + n;
     a.ld[i] = float2{a.lse[i] * kLog2e, s};
   }
-  if (a.zero_uncovered) {
+  const bool pad = n >= batch_len(a.lengths, b, a.N);  // past this batch's length
+  if (a.zero_uncovered || pad) {
     bool kept = false;
     for (int p = 0; p < a.P; ++p) kept |= (n % a.r_all[p]) == (h % a.r_all[p]);
-    if (!kept) {
+    if (!kept || pad) {
       zero8((T*)a.dq + off);
       zero8((T*)a.dk + off);
       zero8((T*)a.dv + off);
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdFinalizeArgs
   const uint32_t n = (blockIdx.x - b * a.nblk) * 32 + (threadIdx.x >> 3);
   const int c = threadIdx.x & 7;
   const uint32_t h = blockIdx.y;
-  if (n >= (uint32_t)a.N) return;
+  if (n >= (uint32_t)batch_len(a.lengths, b, a.N)) return;  // padding rows were zeroed
   uint32_t kept = 0;
   int cnt = 0;
   uint32_t sp[kMaxP];
@@ -151,6 +152,7 @@ __global__ __launch_bounds__(256) void bwd_finalize_class_kernel(const BwdFinali
   if (t >= a.rows_per_class) return;
   const int c = threadIdx.x & 7;
   const uint32_t n = rho + a.R * t;
+  if (n >= (uint32_t)batch_len(a.lengths, b, a.N)) return;  // padding rows were zeroed
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t out_off = (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
   float acc[3][8];

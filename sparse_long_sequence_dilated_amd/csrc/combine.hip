@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const uint32_t n = (blockIdx.x - b * a.nblk) * 32 + (threadIdx.x >> 3);
   const int c = threadIdx.x & 7;
   const uint32_t h = blockIdx.y;
-  if (n >= (uint32_t)a.N) return;
+  if (n >= (uint32_t)batch_len(a.lengths, b, a.N)) return;  // padding: see pad_rows_kernel
 
   uint32_t kept = 0, sidx[NP];
 #pragma unroll
@@ -162,6 +162,7 @@ __global__ __launch_bounds__(256) void combine_class_kernel(const CombineArgs a)
   if (t >= a.rows_per_class) return;
   const int c = threadIdx.x & 7;
   const uint32_t n = rho + a.R * t;
+  if (n >= (uint32_t)batch_len(a.lengths, b, a.N)) return;  // padding: see pad_rows_kernel
   const int64_t bh = (int64_t)b * a.H + h;
   T* orow = (T*)a.o + (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
   float* lse_dst = a.lse + bh * a.N + n;
@@ -248,6 +249,31 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t stream) {
     launch_combine_np<float>(a, grid, stream);
   else
     launch_combine_np<__bf16>(a, grid, stream);
+  return hipGetLastError();
+}
+
+// Rows past a batch's length are padding: output 0, log-sum-exp -inf.
+// 32 rows of one (batch, head) per workgroup, 8 lanes per row.
+template <typename T>
+__global__ __launch_bounds__(256) void pad_rows_kernel(const CombineArgs a) {
+  const uint32_t b = blockIdx.x / a.nblk;
+  const uint32_t n = (blockIdx.x - b * a.nblk) * 32 + (threadIdx.x >> 3);
+  const int c = threadIdx.x & 7;
+  const uint32_t h = blockIdx.y;
+  if (n >= (uint32_t)a.N || n < (uint32_t)batch_len(a.lengths, b, a.N)) return;
+  float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  Vec8<T>::store((T*)a.o + (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c, zero);
+  if (c == 0) a.lse[((int64_t)b * a.H + h) * a.N + n] = -INFINITY;
+}
+
+hipError_t launch_pad_rows(const CombineArgs& a, int dtype, hipStream_t stream) {
+  if (a.B * a.N * a.H == 0 || !a.lengths) return hipSuccess;
+  const dim3 grid((unsigned)(a.B * a.nblk), (unsigned)a.H);
+  TimedLaunch tl("combine", stream);
+  if (dtype == DLA_F32)
+    hipLaunchKernelGGL(pad_rows_kernel<float>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(pad_rows_kernel<__bf16>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

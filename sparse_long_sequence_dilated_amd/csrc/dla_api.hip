@@ -45,7 +45,7 @@ static void fill_fwd_args(const Plan& pl, AttnFwdArgs* a) {
 // Attention pass and merge for a validated plan (whole sequence or shard).
 static int forward_impl(const Plan& pl, const void* q, const void* k, const void* v,
                         const void* const* ext_k, const void* const* ext_v, void* o, float* lse,
-                        void* ws, size_t ws_bytes, void* stream) {
+                        void* ws, size_t ws_bytes, void* stream, const int32_t* lengths = nullptr) {
   int rc;
   if (pl.empty) return DLA_OK;  // nothing is read or written; pointers may be null
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
@@ -61,6 +61,7 @@ static int forward_impl(const Plan& pl, const void* q, const void* k, const void
   a.v = v;
   a.o = o;
   a.lse = lse;
+  a.lengths = lengths;
   fill_fwd_args(pl, &a);
   for (int i = 0; i < pl.P; ++i) {
     if (!pl.span[i]) continue;
@@ -80,10 +81,11 @@ static int forward_impl(const Plan& pl, const void* q, const void* k, const void
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = pl.dtype == DLA_BF16 ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_f32(a, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (pl.need_combine) {
+  if (pl.need_combine || lengths) {
     CombineArgs cb{};
     cb.o = o;
     cb.lse = lse;
+    cb.lengths = lengths;
     for (int i = 0; i < pl.P; ++i) {
       cb.part_o[i] = a.part_o[i];
       cb.part_lse[i] = a.part_lse[i];
@@ -120,8 +122,12 @@ static int forward_impl(const Plan& pl, const void* q, const void* k, const void
       cb.R = (uint32_t)R;
       cb.rows_per_class = (uint32_t)rpc;
     }
-    e = launch_combine(cb, pl.dtype, st);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    if (pl.need_combine) {
+      e = launch_combine(cb, pl.dtype, st);
+      if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
+    e = launch_pad_rows(cb, pl.dtype, st);  // rows past a batch's length
+    if (e != hipSuccess) return hip_fail(e, "padding launch");
   }
   return DLA_OK;
 }
@@ -138,6 +144,19 @@ extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const v
   int rc = make_plan(desc, shape, &pl);
   if (rc) return rc;
   return forward_impl(pl, q, k, v, nullptr, nullptr, o, lse, ws, ws_bytes, stream);
+}
+
+extern "C" int dla_forward_varlen(const dla_desc* desc, const dla_shape* shape,
+                                  const int32_t* lengths, const void* q, const void* k,
+                                  const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  clear_error();
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl);
+  if (rc) return rc;
+  if (!pl.empty && (!lengths || ((uintptr_t)lengths & 3u)))
+    return fail(DLA_E_INVALID, "lengths is null or not 4-byte aligned");
+  return forward_impl(pl, q, k, v, nullptr, nullptr, o, lse, ws, ws_bytes, stream, lengths);
 }
 
 extern "C" int dla_forward_shard(const dla_desc* desc, const dla_shape* shape,

@@ -48,8 +48,10 @@ static void residue_classes(const Plan& pl, uint32_t* R_out, uint32_t* rpc_out) 
 }
 
 static hipError_t run_prep(const Plan& pl, const void* o, const float* lse, const void* dout,
-                           float2* ld, void* dq, void* dk, void* dv, hipStream_t st) {
+                           float2* ld, void* dq, void* dk, void* dv, hipStream_t st,
+                           const int32_t* lengths = nullptr) {
   BwdPrepArgs pa{};
+  pa.lengths = lengths;
   pa.o = o;
   pa.dout = dout;
   pa.lse = lse;
@@ -74,8 +76,9 @@ static hipError_t run_prep(const Plan& pl, const void* o, const float* lse, cons
 // of the patterns keeping a row.
 static int run_attention(const Plan& pl, const void* q, const void* k, const void* v,
                          const void* dout, const float2* ld, char* wsb, void* dq, void* dk,
-                         void* dv, hipStream_t st) {
+                         void* dv, hipStream_t st, const int32_t* lengths = nullptr) {
   AttnBwdArgs a{};
+  a.lengths = lengths;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -114,8 +117,10 @@ static int run_attention(const Plan& pl, const void* q, const void* k, const voi
   return DLA_OK;
 }
 
-static int run_finalize(const Plan& pl, char* wsb, void* dq, void* dk, void* dv, hipStream_t st) {
+static int run_finalize(const Plan& pl, char* wsb, void* dq, void* dk, void* dv, hipStream_t st,
+                        const int32_t* lengths = nullptr) {
   BwdFinalizeArgs f{};
+  f.lengths = lengths;
   for (int i = 0; i < pl.P; ++i) {
     for (int g = 0; g < 3; ++g) f.part[i][g] = (const float*)(wsb + pl.part_g_off[i][g]);
     f.r[i] = pl.r[i];
@@ -140,14 +145,10 @@ static int run_finalize(const Plan& pl, char* wsb, void* dq, void* dk, void* dv,
   return DLA_OK;
 }
 
-extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const void* q,
-                            const void* k, const void* v, const void* o, const float* lse,
-                            const void* dout, void* dq, void* dk, void* dv, void* ws,
-                            size_t ws_bytes, void* stream) {
-  clear_error();
-  Plan pl;
-  int rc = make_plan(desc, shape, &pl);
-  if (rc) return rc;
+static int backward_impl(const Plan& pl, const int32_t* lengths, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
   if (pl.empty) return DLA_OK;  // nothing is read or written; pointers may be null
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
       (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse")) || (rc = check_ptr(dout, "dout")) ||
@@ -161,11 +162,36 @@ extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const 
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
   float2* ld = (float2*)(wsb + pl.ld_off);
-  hipError_t e = run_prep(pl, o, lse, dout, ld, dq, dk, dv, st);
+  hipError_t e = run_prep(pl, o, lse, dout, ld, dq, dk, dv, st, lengths);
   if (e != hipSuccess) return hip_fail(e, "backward preprocessing launch");
-  if ((rc = run_attention(pl, q, k, v, dout, ld, wsb, dq, dk, dv, st))) return rc;
-  if (pl.need_finalize && (rc = run_finalize(pl, wsb, dq, dk, dv, st))) return rc;
+  if ((rc = run_attention(pl, q, k, v, dout, ld, wsb, dq, dk, dv, st, lengths))) return rc;
+  if (pl.need_finalize && (rc = run_finalize(pl, wsb, dq, dk, dv, st, lengths))) return rc;
   return DLA_OK;
+}
+
+extern "C" int dla_backward(const dla_desc* desc, const dla_shape* shape, const void* q,
+                            const void* k, const void* v, const void* o, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl);
+  if (rc) return rc;
+  return backward_impl(pl, nullptr, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+extern "C" int dla_backward_varlen(const dla_desc* desc, const dla_shape* shape,
+                                   const int32_t* lengths, const void* q, const void* k,
+                                   const void* v, const void* o, const float* lse,
+                                   const void* dout, void* dq, void* dk, void* dv, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl);
+  if (rc) return rc;
+  if (!pl.empty && (!lengths || ((uintptr_t)lengths & 3u)))
+    return fail(DLA_E_INVALID, "lengths is null or not 4-byte aligned");
+  return backward_impl(pl, lengths, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream);
 }
 
 // One spanning pattern p of a shard: its segment contiguous per (batch,

@@ -25,6 +25,13 @@ __device__ __forceinline__ int64_t seg_base_row(int64_t seg, int w, int r, int h
   return seg * (int64_t)w + (h % r);
 }
 
+// Length of batch b's sequence: lengths[b] clamped to [0, N], or N.
+__device__ __forceinline__ int64_t batch_len(const int32_t* lengths, int64_t b, int64_t N) {
+  if (!lengths) return N;
+  const int64_t x = lengths[b];
+  return x < 0 ? 0 : (x > N ? N : x);
+}
+
 // Sparse rows of segment seg for head h: L_full = w/r, or fewer in a last
 // segment that the end of the sequence cuts short (rows (h mod r) + a*r
 // below the N - seg*w rows that remain).

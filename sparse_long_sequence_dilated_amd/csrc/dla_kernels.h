@@ -35,6 +35,7 @@ struct AttnFwdArgs {
   const void* ext_k[kMaxP];
   const void* ext_v[kMaxP];
   Schedule sched;
+  const int32_t* lengths;  // per-batch sequence lengths (device), null: all N
 };
 
 // Merge of the per-pattern results into o/lse.
@@ -54,6 +55,7 @@ struct CombineArgs {
   // rates share the set of patterns that keep them.
   uint32_t R;              // 0: per-row launch
   uint32_t rows_per_class; // N / R
+  const int32_t* lengths;  // per-batch sequence lengths (device), null: all N
 };
 
 // One device's part of the key/value exchange of a spanning pattern.
@@ -129,6 +131,7 @@ struct AttnBwdArgs {
   // and dQ partials hold nsp_q rows per (batch, head).
   int qlo, qhi;
   int64_t nsp_q;
+  const int32_t* lengths;  // per-batch sequence lengths (device), null: all N
 };
 
 // Sum of the per-pattern partial gradients of rows kept by several patterns.
@@ -145,6 +148,7 @@ struct BwdFinalizeArgs {
   uint32_t R;              // residue-class launch: R = lcm of the rates (0: per row)
   uint32_t rows_per_class; // N / R
   uint32_t span_mask;      // sequence shard: patterns whose segments span devices
+  const int32_t* lengths;  // per-batch sequence lengths (device), null: all N
 };
 
 struct BwdPrepArgs {
@@ -160,6 +164,7 @@ struct BwdPrepArgs {
   int P;
   int r_all[kMaxP];
   int zero_uncovered;      // write zero gradients for rows no pattern keeps
+  const int32_t* lengths;  // per-batch sequence lengths (device), null: all N
 };
 
 // Scope guard of the opt-in launch timing (dla_timing_enable): records HIP
@@ -180,6 +185,7 @@ class TimedLaunch {
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream);
 hipError_t launch_shard_gather(const ShardGatherArgs& a, hipStream_t stream);
+hipError_t launch_pad_rows(const CombineArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_shard_ld(const ShardLdArgs& a, hipStream_t stream);
 hipError_t launch_shard_relayout(const ShardRelayoutArgs& a, hipStream_t stream);
 hipError_t launch_shard_finish(const ShardFinishArgs& a, hipStream_t stream);

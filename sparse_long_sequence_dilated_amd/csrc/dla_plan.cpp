@@ -266,6 +266,28 @@ int dla_pair_count_shard(const dla_desc* desc, const dla_shape* shape, const dla
   return DLA_OK;
 }
 
+int dla_pair_count_varlen(const dla_desc* desc, const dla_shape* shape, const int32_t* lengths,
+                          int64_t* pairs) {
+  dla::Plan p;
+  int rc = dla::make_plan(desc, shape, &p);
+  if (rc != DLA_OK) return rc;
+  if (!pairs) return dla::fail(DLA_E_INVALID, "null output pointer");
+  if (!lengths && shape->B > 0) return dla::fail(DLA_E_INVALID, "null lengths");
+  int64_t total = 0;
+  for (int64_t b = 0; b < shape->B; ++b) {
+    const int64_t n = lengths[b] < 0 ? 0 : (lengths[b] > shape->N ? shape->N : lengths[b]);
+    if (n == 0) continue;
+    dla_shape one = *shape;
+    one.B = 1;
+    one.N = n;
+    if ((rc = dla::make_plan(desc, &one, &p)) != DLA_OK) return rc;
+    if (__builtin_add_overflow(total, p.pairs, &total))
+      return dla::fail(DLA_E_UNSUPPORTED, "the number of attention pairs exceeds 2^63");
+  }
+  *pairs = total;
+  return DLA_OK;
+}
+
 int dla_pair_count(const dla_desc* desc, const dla_shape* shape, int64_t* pairs) {
   dla::Plan p;
   const int rc = dla::make_plan(desc, shape, &p);

@@ -26,7 +26,8 @@ HEAD_DIM = 64
 
 EXPORTS = ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
            "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather", "dla_forward_shard",
-           "dla_backward_shard", "dla_shard_finish",
+           "dla_backward_shard", "dla_shard_finish", "dla_forward_varlen", "dla_backward_varlen",
+           "dla_pair_count_varlen",
            "dla_timing_enable", "dla_timing_collect", "dla_strerror", "dla_last_error")
 
 
@@ -84,6 +85,9 @@ def lib():
     L.dla_backward_shard.argtypes = [pd, ps, psh, vp, vp, vp, vp, vp, vp, pvp, pvp, vp, vp, vp, pvp, pvp,
                                      vp, sz, vp]
     L.dla_shard_finish.argtypes = [pd, ps, psh, pvp, pvp, vp, vp, vp, sz, vp]
+    L.dla_forward_varlen.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dla_backward_varlen.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dla_pair_count_varlen.argtypes = [pd, ps, ctypes.POINTER(i32), ctypes.POINTER(i64)]
     L.dla_timing_enable.argtypes = [ctypes.c_int]
     L.dla_timing_enable.restype = ctypes.c_int
     L.dla_timing_collect.argtypes = [ctypes.c_char_p, ctypes.POINTER(i64),
@@ -95,7 +99,8 @@ def lib():
     L.dla_last_error.restype = ctypes.c_char_p
     for name in ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
                  "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather",
-                 "dla_forward_shard", "dla_backward_shard", "dla_shard_finish"):
+                 "dla_forward_shard", "dla_backward_shard", "dla_shard_finish",
+                 "dla_forward_varlen", "dla_backward_varlen", "dla_pair_count_varlen"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -413,3 +418,72 @@ def finish_shard(dk, dv, patterns, total_rows, shard_start, red_dk, red_dv, work
                                   dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                   _stream(stream, dk.device)))
     return dk, dv
+
+
+# ---- batches of different lengths ----
+
+def _lengths_tensor(lengths, B, device):
+    import torch
+    t = torch.as_tensor(lengths, dtype=torch.int32)
+    if t.shape != (B,):
+        raise DlaError(DLA_E_INVALID, f"lengths must have B = {B} entries")
+    return t.to(device).contiguous()
+
+
+def forward_varlen(q, k, v, lengths, patterns, causal=True, scale=None, out=None, lse=None,
+                   workspace=None, stream=None):
+    """Forward on a padded batch: batch b is its first lengths[b] rows; returns (o, lse)."""
+    import torch
+    scale = default_scale(q.shape[-1]) if scale is None else scale
+    _same_layout(q, k, v)
+    shape = _shape_of(q)
+    desc = make_desc(patterns, causal, scale)
+    ws_f = ctypes.c_size_t(0)
+    _check(lib().dla_plan_check(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(ws_f), None))
+    B, N, H, _ = q.shape
+    lt = _lengths_tensor(lengths, B, q.device)
+    o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
+    _same_layout(q, o)
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        workspace = torch.empty(max(ws_f.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().dla_forward_varlen(ctypes.byref(desc), ctypes.byref(shape), lt.data_ptr(), q.data_ptr(),
+                                    k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(), _stream(stream, q.device)))
+    return o, lse_t
+
+
+def backward_varlen(q, k, v, o, lse, dout, lengths, patterns, causal=True, scale=None, dq=None,
+                    dk=None, dv=None, workspace=None, stream=None):
+    """Gradients on a padded batch (padding rows get zero gradients)."""
+    import torch
+    scale = default_scale(q.shape[-1]) if scale is None else scale
+    _same_layout(q, k, v, o, dout)
+    shape = _shape_of(q)
+    desc = make_desc(patterns, causal, scale)
+    ws_b = ctypes.c_size_t(0)
+    _check(lib().dla_plan_check(ctypes.byref(desc), ctypes.byref(shape), None, ctypes.byref(ws_b)))
+    lt = _lengths_tensor(lengths, q.shape[0], q.device)
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        _same_layout(q, g)
+        grads.append(g)
+    if workspace is None:
+        workspace = torch.empty(max(ws_b.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().dla_backward_varlen(ctypes.byref(desc), ctypes.byref(shape), lt.data_ptr(), q.data_ptr(),
+                                     k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                                     grads[2].data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                     _stream(stream, q.device)))
+    return tuple(grads)
+
+
+def pair_count_varlen(patterns, causal, lengths, N, H):
+    d = make_desc(patterns, causal, 1.0)
+    s = make_shape(len(lengths), N, H, HEAD_DIM, DLA_BF16)
+    arr = (ctypes.c_int32 * max(1, len(lengths)))(*[int(x) for x in lengths])
+    out = ctypes.c_int64(0)
+    _check(lib().dla_pair_count_varlen(ctypes.byref(d), ctypes.byref(s), arr, ctypes.byref(out)))
+    return out.value

@@ -218,3 +218,12 @@ def test_geometric_workloads_have_linear_work():
     p4 = dla.pair_count(c4.patterns, True, 1, c4.N, 12) / (c4.N * 12)
     assert 1900 < p3 < p4 < 2049
     assert np.isclose(p3, 1024.5 * sum(2.0 ** -i for i in range(5)))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_pair_count_varlen_matches_oracle(causal):
+    pats = ((256, 1), (512, 2), (2048, 4))
+    lens = (1000, 0, 37, 1024, 5000)          # 5000 is clamped to N
+    N = 1024
+    want = oracle.pair_count(len(lens), N, 3, pats, causal, lengths=[min(x, N) for x in lens])
+    assert dla.pair_count_varlen(pats, causal, lens, N, 3) == want
