@@ -14,6 +14,9 @@ Also reported, as extra fields of the same line:
     over 8 devices (the last shard, whose segments of the three coarsest
     patterns span 2, 4 and 8 devices): its exchange parts and its forward,
     and (`fwd_bwd`) forward plus backward, the collectives excluded;
+  * `layer`: the attention layer around the operator (hipBLASLt projections,
+    768 dimensions, 12 heads, random weights) at 16 x 2K and 1 x 32K tokens,
+    forward and forward plus backward;
   * `roofline` of the kernel family that takes most of the timed region,
     timed live with HIP events around its launches on the launch stream;
   * `cpu_baseline`: the CPU oracle (float32, thread pool) on a bounded
@@ -251,6 +254,53 @@ def cpu_baseline(wl, heads=4):
                        f"{workers} threads, {t:.2f} s wall; scaled by {scale:g} to the full workload")}
 
 
+def layer_bench(B, N, steps, warmup):
+    """The attention layer (Q/K/V projections, dilated attention, output
+    projection; random weights) at 768 dimensions and 12 heads with the 32K
+    pattern set: forward, and forward plus backward, per step."""
+    import torch
+    from sparse_long_sequence_dilated_amd import dla, inputs
+    H, D = 12, 64
+    E = H * D
+    pats = inputs.geometric_patterns(2048, 2, 5)
+    scale = 1.0 / math.sqrt(D)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3000 + N)
+    x = torch.randn((B, N, E), device="cuda", generator=g).bfloat16()
+    dy = torch.randn_like(x)
+    w_qkv = (torch.randn((E, 3 * E), device="cuda", generator=g) / math.sqrt(E)).bfloat16()
+    w_o = (torch.randn((E, E), device="cuda", generator=g) / math.sqrt(E)).bfloat16()
+    blas = dla.Blas()
+    ws_f, ws_b = dla.layer_plan_check(pats, True, scale, B, N, H)
+    wsf = torch.empty(ws_f, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
+    saved = {}
+
+    def fstep():
+        saved["f"] = dla.layer_forward(x, w_qkv, w_o, pats, blas, True, scale, workspace=wsf)
+
+    def bstep():
+        fstep()
+        _, qkv, attn, lse = saved["f"]
+        dla.layer_backward(x, w_qkv, w_o, qkv, attn, lse, dy, pats, blas, True, scale, workspace=wsb)
+
+    pairs = dla.pair_count(pats, True, B, N, H)
+    gemm_flops = 8 * B * N * E * E
+    out = {"workload": f"attention layer E={E} H={H} (random weights), bf16, B={B}, N={N}, "
+                       f"causal, patterns {[list(p) for p in pats]}"}
+    for name, fn, mult in (("forward", fstep, 1), ("fwd_bwd", bstep, 3)):
+        ms, fams = time_steps(fn, steps, warmup)
+        attn_ms = sum(t for _, t in fams.values()) / steps
+        flops = mult * gemm_flops + (4 if mult == 1 else 14) * D * pairs
+        out[name] = {"tokens_per_s": B * N / (ms * 1e-3), "ms": ms,
+                     "useful_tflops": flops / (ms * 1e-3) / 1e12,
+                     "attention_kernels_ms": attn_ms, "rest_ms": ms - attn_ms}
+    blas.close()
+    del x, dy, w_qkv, w_o, wsf, wsb, saved
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +378,8 @@ def main():
         extra.append(forward_only("C3", max(5, args.steps), args.warmup))
         extra.append(forward_only("C4", max(3, args.steps // 4), 1))
         shard = shard_forward("C4", 8, 7, max(3, args.steps // 2), 1)
+        layers = [layer_bench(16, 2048, max(5, args.steps // 2), 2),
+                  layer_bench(1, 32768, max(5, args.steps // 2), 2)]
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
     line = {
@@ -342,6 +394,7 @@ def main():
     }
     if not args.no_forward_lines:
         line["shard_forward"] = shard
+        line["layer"] = layers
     print(json.dumps(line), flush=True)
 
 

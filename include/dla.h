@@ -283,6 +283,47 @@ int dla_shard_finish(const dla_desc* desc, const dla_shape* shape, const dla_sha
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---- A LongNet attention layer ([G] 实验设计: 768-dimensional model,
+ * 12 heads) ----
+ *
+ * Y = DA(X W_q, X W_k, X W_v) W_o with W_qkv = [W_q | W_k | W_v], no bias,
+ * E = 64 H model dimensions.  X, Y [B, N, E] bf16 contiguous; W_qkv [E, 3E]
+ * and W_o [E, E] bf16 row-major (y = x W).  The projections are plain GEMMs
+ * done by hipBLASLt (fp32 accumulation) with the caller's handle
+ * (dla_blas_create); the attention is dla_forward / dla_backward.
+ */
+
+/* Create / destroy the hipBLASLt handle the layer calls use (the only calls
+ * that allocate: hipBLASLt's own host and device state). */
+int dla_blas_create(void** handle);
+int dla_blas_destroy(void* handle);
+
+/* Workspace bytes of dla_layer_forward and dla_layer_backward.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED. */
+int dla_layer_plan_check(const dla_desc* desc, int64_t B, int64_t N, int64_t H,
+                         size_t* ws_fwd_bytes, size_t* ws_bwd_bytes);
+
+/*
+ * Forward.  Writes qkv ([3, B, N, H, D] bf16: q, k, v, each contiguous), the
+ * attention output attn ([B, N, H, D] bf16) and lse ([B, H, N] fp32), which
+ * the backward reads, and y.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_WORKSPACE, DLA_E_HIP.
+ */
+int dla_layer_forward(const dla_desc* desc, int64_t B, int64_t N, int64_t H, const void* x,
+                      const void* w_qkv, const void* w_o, void* qkv, void* attn, float* lse,
+                      void* y, void* blas, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of sum(dy * y): dx ([B, N, E] bf16), dw_qkv ([E, 3E] fp32) and
+ * dw_o ([E, E] fp32), from the forward's x, weights, qkv, attn and lse.
+ * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED, DLA_E_WORKSPACE, DLA_E_HIP.
+ */
+int dla_layer_backward(const dla_desc* desc, int64_t B, int64_t N, int64_t H, const void* x,
+                       const void* w_qkv, const void* w_o, const void* qkv, const void* attn,
+                       const float* lse, const void* dy, void* dx, float* dw_qkv, float* dw_o,
+                       void* blas, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Opt-in launch timing, a profiling aid.  While enabled (on != 0), every
  * kernel launch made by dla_forward / dla_backward is bracketed by two HIP
  * events recorded on the caller's stream (host-side bookkeeping only; the

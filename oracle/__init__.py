@@ -6,7 +6,9 @@ leg may import this package.
 from .dilated import (backward, brute_force_forward, check_patterns, combine, forward,
                       forward_rows, multiplicity, pair_count, row_map, segment_attention,
                       segment_rows, segments, useful_flops)
+from .layer import layer_backward, layer_forward, layer_forward_rows
 
 __all__ = ["backward", "brute_force_forward", "check_patterns", "combine", "forward",
            "forward_rows", "multiplicity", "pair_count", "row_map", "segment_attention",
-           "segment_rows", "segments", "useful_flops"]
+           "segment_rows", "segments", "useful_flops", "layer_backward", "layer_forward",
+           "layer_forward_rows"]

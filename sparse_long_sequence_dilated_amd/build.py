@@ -31,7 +31,8 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 HOST_SOURCES = ["dla_plan.cpp"]
 HIP_SOURCES = ["dla_api.hip", "dla_bwd_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
                "combine.hip", "attn_bwd_bf16.hip", "bwd_misc.hip", "dla_timing.hip",
-               "shard.hip"]
+               "shard.hip", "dla_layer.hip"]
+LINK_FLAGS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def _run(cmd):
@@ -58,7 +59,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, *LINK_FLAGS, "-o", tmp])
     shutil.move(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(sources)} sources")

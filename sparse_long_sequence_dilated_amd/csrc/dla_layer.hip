@@ -1,0 +1,235 @@
+// A LongNet attention layer around the operator: Q = X W_q, K = X W_k,
+// V = X W_v (W_qkv = [W_q | W_k | W_v]), dilated attention A = DA(Q, K, V),
+// and Y = A W_o, with random weights at the pages' model settings (the
+// gptget.net LongNet summary, section 实验设计: 768-dimensional model, 12
+// heads).  The projections are plain GEMMs and go to hipBLASLt; the attention
+// runs through dla_forward / dla_backward.  q, k, v (and their gradients)
+// live in one [3, B, N, H, D] buffer, each contiguous like the attention
+// output, so that all eight attention tensors share one layout.
+//
+// Row-major C[M, N] = op(A)[M, K] op(B)[K, N] is the column-major product
+// C^T = op(B)^T op(A)^T, which is how the calls below are issued.
+#include <hipblaslt/hipblaslt.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "dla_device.h"
+
+using namespace dla;
+
+namespace {
+
+int check(const void* p, const char* name) {
+  if (!p) return fail(DLA_E_INVALID, "%s is null", name);
+  if ((uintptr_t)p & 15u) return fail(DLA_E_INVALID, "%s is not 16-byte aligned", name);
+  return DLA_OK;
+}
+
+#define DLA_BLAS(call)                                                                  \
+  do {                                                                                  \
+    const hipblasStatus_t s_ = (call);                                                  \
+    if (s_ != HIPBLAS_STATUS_SUCCESS) {                                                 \
+      rc = fail(DLA_E_HIP, "hipBLASLt %s failed with status %d", #call, (int)s_);        \
+      goto done;                                                                        \
+    }                                                                                   \
+  } while (0)
+
+// Row-major C = op(A) op(B) + beta C, A and B bf16, C bf16 or fp32, fp32
+// accumulation.  A is [M, K] (or [K, M] with ta), B is [K, N] (or [N, K]),
+// C is [M, N]; lda, ldb, ldc are their row-major leading dimensions.
+int gemm_rm(hipblasLtHandle_t h, hipStream_t st, void* ws, size_t ws_bytes, bool ta, bool tb,
+            int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+            int64_t ldb, void* C, int64_t ldc, hipDataType ctype, float beta) {
+  int rc = DLA_OK;
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  hipblasLtMatmulHeuristicResult_t heur{};
+  int found = 0;
+  const float alpha = 1.f;
+  // column-major operands: first = B (as op(B)^T), second = A (as op(A)^T)
+  const hipblasOperation_t op1 = tb ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+  const hipblasOperation_t op2 = ta ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+  const uint64_t wsb = ws_bytes;
+  DLA_BLAS(hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F));
+  DLA_BLAS(hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &op1, sizeof(op1)));
+  DLA_BLAS(hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &op2, sizeof(op2)));
+  DLA_BLAS(hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, tb ? K : N, tb ? N : K, ldb));
+  DLA_BLAS(hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, ta ? M : K, ta ? K : M, lda));
+  DLA_BLAS(hipblasLtMatrixLayoutCreate(&lc, ctype, N, M, ldc));
+  DLA_BLAS(hipblasLtMatmulPreferenceCreate(&pref));
+  DLA_BLAS(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                 &wsb, sizeof(wsb)));
+  DLA_BLAS(hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, 1, &heur, &found));
+  if (found < 1) {
+    rc = fail(DLA_E_UNSUPPORTED, "hipBLASLt has no algorithm for a %lldx%lldx%lld product",
+              (long long)M, (long long)N, (long long)K);
+    goto done;
+  }
+  DLA_BLAS(hipblasLtMatmul(h, desc, &alpha, B, la, A, lb, &beta, C, lc, C, lc, &heur.algo, ws, ws_bytes,
+                           st));
+done:
+  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+  if (lc) hipblasLtMatrixLayoutDestroy(lc);
+  if (lb) hipblasLtMatrixLayoutDestroy(lb);
+  if (la) hipblasLtMatrixLayoutDestroy(la);
+  if (desc) hipblasLtMatmulDescDestroy(desc);
+  return rc;
+}
+#undef DLA_BLAS
+
+constexpr size_t kGemmWs = (size_t)32 << 20;  // hipBLASLt workspace in the caller's buffer
+
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* src, __bf16* dst, int64_t n) {
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (int64_t)gridDim.x * 256 * 8) {
+    const float4 a = *(const float4*)(src + i), b = *(const float4*)(src + i + 4);
+    *(uint4*)(dst + i) = uint4{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w)};
+  }
+}
+
+// n a multiple of 8 (M * E with E = 64 H)
+hipError_t launch_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_t st) {
+  const int64_t blocks = std::min<int64_t>((n / 8 + 255) / 256, 65536);
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, (__bf16*)dst, n);
+  return hipGetLastError();
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// q, k, v, the attention output and the gradients: contiguous [B, N, H, D].
+dla_shape head_shape(int64_t B, int64_t N, int64_t H) {
+  dla_shape s{};
+  s.B = B;
+  s.N = N;
+  s.H = H;
+  s.D = kD;
+  s.dtype = DLA_BF16;
+  s.stride_h = kD;
+  s.stride_n = H * kD;
+  s.stride_b = N * H * kD;
+  return s;
+}
+
+// Layer workspace: forward = attention workspace + GEMM workspace; backward
+// = dA [M, E] bf16 + dQKV [3, M, E] bf16 + dX [M, E] fp32 + attention
+// backward workspace + GEMM workspace.
+int layer_plan(const dla_desc* desc, int64_t B, int64_t N, int64_t H, size_t* fwd, size_t* bwd) {
+  if (B < 1 || N < 1 || H < 1) return fail(DLA_E_INVALID, "B, N and H must be positive");
+  dla_shape s = head_shape(B, N, H);
+  size_t af = 0, ab = 0;
+  const int rc = dla_plan_check(desc, &s, &af, &ab);
+  if (rc) return rc;
+  const size_t M = (size_t)B * N, E = (size_t)H * kD;
+  if (fwd) *fwd = align256(af) + kGemmWs;
+  if (bwd) *bwd = align256(M * E * 2) + align256(M * 3 * E * 2) + align256(M * E * 4) + align256(ab) + kGemmWs;
+  return DLA_OK;
+}
+
+}  // namespace
+
+extern "C" int dla_blas_create(void** handle) {
+  clear_error();
+  if (!handle) return fail(DLA_E_INVALID, "null handle pointer");
+  hipblasLtHandle_t h = nullptr;
+  const hipblasStatus_t s = hipblasLtCreate(&h);
+  if (s != HIPBLAS_STATUS_SUCCESS) return fail(DLA_E_HIP, "hipblasLtCreate failed with status %d", (int)s);
+  *handle = h;
+  return DLA_OK;
+}
+
+extern "C" int dla_blas_destroy(void* handle) {
+  clear_error();
+  if (handle) hipblasLtDestroy((hipblasLtHandle_t)handle);
+  return DLA_OK;
+}
+
+extern "C" int dla_layer_plan_check(const dla_desc* desc, int64_t B, int64_t N, int64_t H,
+                                    size_t* ws_fwd_bytes, size_t* ws_bwd_bytes) {
+  clear_error();
+  return layer_plan(desc, B, N, H, ws_fwd_bytes, ws_bwd_bytes);
+}
+
+extern "C" int dla_layer_forward(const dla_desc* desc, int64_t B, int64_t N, int64_t H,
+                                 const void* x, const void* w_qkv, const void* w_o, void* qkv,
+                                 void* attn, float* lse, void* y, void* blas, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  clear_error();
+  size_t need = 0;
+  int rc = layer_plan(desc, B, N, H, &need, nullptr);
+  if (rc) return rc;
+  if ((rc = check(x, "x")) || (rc = check(w_qkv, "w_qkv")) || (rc = check(w_o, "w_o")) ||
+      (rc = check(qkv, "qkv")) || (rc = check(attn, "attn")) || (rc = check(lse, "lse")) ||
+      (rc = check(y, "y")) || (rc = check(ws, "workspace")))
+    return rc;
+  if (!blas) return fail(DLA_E_INVALID, "blas handle is null");
+  if (ws_bytes < need) return fail(DLA_E_WORKSPACE, "layer workspace needs %zu bytes, got %zu", need, ws_bytes);
+  hipblasLtHandle_t h = (hipblasLtHandle_t)blas;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t M = B * N, E = H * kD;
+  char* gws = (char*)ws + (need - kGemmWs);
+  // Q, K, V = X W_q, X W_k, X W_v (column blocks of W_qkv)
+  char* qb = (char*)qkv;
+  for (int j = 0; j < 3; ++j)
+    if ((rc = gemm_rm(h, st, gws, kGemmWs, false, false, M, E, E, x, E, (const __bf16*)w_qkv + j * E,
+                      3 * E, qb + (size_t)j * M * E * 2, E, HIP_R_16BF, 0.f)))
+      return rc;
+  // A = DA(Q, K, V)
+  const dla_shape s = head_shape(B, N, H);
+  if ((rc = dla_forward(desc, &s, qb, qb + (size_t)M * E * 2, qb + (size_t)2 * M * E * 2, attn, lse, ws,
+                        need - kGemmWs, stream)))
+    return rc;
+  // Y = A W_o
+  return gemm_rm(h, st, gws, kGemmWs, false, false, M, E, E, attn, E, w_o, E, y, E, HIP_R_16BF, 0.f);
+}
+
+extern "C" int dla_layer_backward(const dla_desc* desc, int64_t B, int64_t N, int64_t H,
+                                  const void* x, const void* w_qkv, const void* w_o,
+                                  const void* qkv, const void* attn, const float* lse,
+                                  const void* dy, void* dx, float* dw_qkv, float* dw_o, void* blas,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  size_t need = 0;
+  int rc = layer_plan(desc, B, N, H, nullptr, &need);
+  if (rc) return rc;
+  if ((rc = check(x, "x")) || (rc = check(w_qkv, "w_qkv")) || (rc = check(w_o, "w_o")) ||
+      (rc = check(qkv, "qkv")) || (rc = check(attn, "attn")) || (rc = check(lse, "lse")) ||
+      (rc = check(dy, "dy")) || (rc = check(dx, "dx")) || (rc = check(dw_qkv, "dw_qkv")) ||
+      (rc = check(dw_o, "dw_o")) || (rc = check(ws, "workspace")))
+    return rc;
+  if (!blas) return fail(DLA_E_INVALID, "blas handle is null");
+  if (ws_bytes < need) return fail(DLA_E_WORKSPACE, "layer workspace needs %zu bytes, got %zu", need, ws_bytes);
+  hipblasLtHandle_t h = (hipblasLtHandle_t)blas;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t M = B * N, E = H * kD;
+  char* da = (char*)ws;                                         // dA [M, E] bf16
+  char* dqkv = da + align256((size_t)M * E * 2);                // dQ, dK, dV [3, M, E] bf16
+  char* dxf = dqkv + align256((size_t)M * 3 * E * 2);           // dX [M, E] fp32
+  char* aws = dxf + align256((size_t)M * E * 4);                // attention backward workspace
+  const size_t aws_bytes = need - kGemmWs - (size_t)(aws - (char*)ws);
+  char* gws = (char*)ws + (need - kGemmWs);
+  // dA = dY W_o^T, dW_o = A^T dY
+  if ((rc = gemm_rm(h, st, gws, kGemmWs, false, true, M, E, E, dy, E, w_o, E, da, E, HIP_R_16BF, 0.f)))
+    return rc;
+  if ((rc = gemm_rm(h, st, gws, kGemmWs, true, false, E, E, M, attn, E, dy, E, dw_o, E, HIP_R_32F, 0.f)))
+    return rc;
+  // dQ, dK, dV
+  const dla_shape s = head_shape(B, N, H);
+  const char* qb = (const char*)qkv;
+  const size_t t = (size_t)M * E * 2;
+  if ((rc = dla_backward(desc, &s, qb, qb + t, qb + 2 * t, attn, lse, da, dqkv, dqkv + t, dqkv + 2 * t,
+                         aws, aws_bytes, stream)))
+    return rc;
+  // dX = sum_j dP_j W_j^T in fp32, rounded once; dW_qkv column blocks = X^T dP_j
+  for (int j = 0; j < 3; ++j)
+    if ((rc = gemm_rm(h, st, gws, kGemmWs, false, true, M, E, E, dqkv + j * t, E,
+                      (const __bf16*)w_qkv + j * E, 3 * E, dxf, E, HIP_R_32F, j ? 1.f : 0.f)))
+      return rc;
+  hipError_t e = launch_f32_to_bf16((const float*)dxf, dx, M * E, st);
+  if (e != hipSuccess) return fail(DLA_E_HIP, "conversion launch: %s", hipGetErrorString(e));
+  for (int j = 0; j < 3; ++j)
+    if ((rc = gemm_rm(h, st, gws, kGemmWs, true, false, E, E, M, x, E, dqkv + j * t, E, dw_qkv + j * E,
+                      3 * E, HIP_R_32F, 0.f)))
+      return rc;
+  return DLA_OK;
+}

@@ -27,7 +27,8 @@ HEAD_DIM = 64
 EXPORTS = ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
            "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather", "dla_forward_shard",
            "dla_backward_shard", "dla_shard_finish", "dla_forward_varlen", "dla_backward_varlen",
-           "dla_pair_count_varlen",
+           "dla_pair_count_varlen", "dla_blas_create", "dla_blas_destroy", "dla_layer_plan_check",
+           "dla_layer_forward", "dla_layer_backward",
            "dla_timing_enable", "dla_timing_collect", "dla_strerror", "dla_last_error")
 
 
@@ -88,6 +89,12 @@ def lib():
     L.dla_forward_varlen.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dla_backward_varlen.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dla_pair_count_varlen.argtypes = [pd, ps, ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    L.dla_blas_create.argtypes = [ctypes.POINTER(vp)]
+    L.dla_blas_destroy.argtypes = [vp]
+    L.dla_layer_plan_check.argtypes = [pd, i64, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.dla_layer_forward.argtypes = [pd, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dla_layer_backward.argtypes = [pd, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     sz, vp]
     L.dla_timing_enable.argtypes = [ctypes.c_int]
     L.dla_timing_enable.restype = ctypes.c_int
     L.dla_timing_collect.argtypes = [ctypes.c_char_p, ctypes.POINTER(i64),
@@ -100,7 +107,9 @@ def lib():
     for name in ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_pair_count",
                  "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather",
                  "dla_forward_shard", "dla_backward_shard", "dla_shard_finish",
-                 "dla_forward_varlen", "dla_backward_varlen", "dla_pair_count_varlen"):
+                 "dla_forward_varlen", "dla_backward_varlen", "dla_pair_count_varlen",
+                 "dla_blas_create", "dla_blas_destroy", "dla_layer_plan_check", "dla_layer_forward",
+                 "dla_layer_backward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -487,3 +496,78 @@ def pair_count_varlen(patterns, causal, lengths, N, H):
     out = ctypes.c_int64(0)
     _check(lib().dla_pair_count_varlen(ctypes.byref(d), ctypes.byref(s), arr, ctypes.byref(out)))
     return out.value
+
+
+# ---- a LongNet attention layer (projections by hipBLASLt, attention by the library) ----
+
+class Blas:
+    """The hipBLASLt handle the layer calls use."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib().dla_blas_create(ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            lib().dla_blas_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def layer_plan_check(patterns, causal, scale, B, N, H):
+    d = make_desc(patterns, causal, scale)
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().dla_layer_plan_check(ctypes.byref(d), B, N, H, ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+def layer_forward(x, w_qkv, w_o, patterns, blas, causal=True, scale=None, workspace=None, stream=None):
+    """Y = DA(X W_q, X W_k, X W_v) W_o; returns (y, qkv, attn, lse) (the last three for the backward)."""
+    import torch
+    B, N, E = x.shape
+    H = E // HEAD_DIM
+    scale = default_scale() if scale is None else scale
+    for t, shp in ((x, (B, N, E)), (w_qkv, (E, 3 * E)), (w_o, (E, E))):
+        if tuple(t.shape) != shp or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise DlaError(DLA_E_INVALID, f"expected a contiguous bfloat16 tensor of shape {shp}")
+    desc = make_desc(patterns, causal, scale)
+    ws_f, _ = layer_plan_check(patterns, causal, scale, B, N, H)
+    qkv = torch.empty((3, B, N, H, HEAD_DIM), dtype=torch.bfloat16, device=x.device)
+    attn = torch.empty((B, N, H, HEAD_DIM), dtype=torch.bfloat16, device=x.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=x.device)
+    y = torch.empty((B, N, E), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(ws_f, dtype=torch.uint8, device=x.device)
+    _check(lib().dla_layer_forward(ctypes.byref(desc), B, N, H, x.data_ptr(), w_qkv.data_ptr(),
+                                   w_o.data_ptr(), qkv.data_ptr(), attn.data_ptr(), lse.data_ptr(),
+                                   y.data_ptr(), blas.handle, workspace.data_ptr(), workspace.numel(),
+                                   _stream(stream, x.device)))
+    return y, qkv, attn, lse
+
+
+def layer_backward(x, w_qkv, w_o, qkv, attn, lse, dy, patterns, blas, causal=True, scale=None,
+                   workspace=None, stream=None):
+    """(dx, dw_qkv, dw_o) of sum(dy * y); weight gradients in float32."""
+    import torch
+    B, N, E = x.shape
+    H = E // HEAD_DIM
+    scale = default_scale() if scale is None else scale
+    desc = make_desc(patterns, causal, scale)
+    _, ws_b = layer_plan_check(patterns, causal, scale, B, N, H)
+    dx = torch.empty_like(x)
+    dw_qkv = torch.empty((E, 3 * E), dtype=torch.float32, device=x.device)
+    dw_o = torch.empty((E, E), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(ws_b, dtype=torch.uint8, device=x.device)
+    _check(lib().dla_layer_backward(ctypes.byref(desc), B, N, H, x.data_ptr(), w_qkv.data_ptr(),
+                                    w_o.data_ptr(), qkv.data_ptr(), attn.data_ptr(), lse.data_ptr(),
+                                    dy.contiguous().data_ptr(), dx.data_ptr(), dw_qkv.data_ptr(),
+                                    dw_o.data_ptr(), blas.handle, workspace.data_ptr(),
+                                    workspace.numel(), _stream(stream, x.device)))
+    return dx, dw_qkv, dw_o

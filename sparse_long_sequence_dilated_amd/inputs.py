@@ -106,3 +106,23 @@ def workload_inputs(wl: Workload, B: int | None = None, N: int | None = None):
 def random_case(seed: int, B: int, N: int, H: int, dtype: str = "f32", count: int = 3, D: int = HEAD_DIM):
     """Small seeded case for property and parity tests."""
     return draw((B, N, H, D), seed, count, dtype)
+
+
+def layer_inputs(seed: int, B: int, N: int, H: int, dtype: str = "bf16", D: int = HEAD_DIM):
+    """(x, w_qkv, w_o, dy) for an attention layer of E = H * D model dimensions.
+
+    x and dy are [B, N, E] standard normal; w_qkv [E, 3E] and w_o [E, E] are
+    standard normal scaled by 1 / sqrt(E) (so that projections of unit-variance
+    rows keep unit variance), all drawn from numpy's PCG64(seed) in that order
+    and, for dtype "bf16", rounded to bfloat16 after scaling.
+    """
+    E = H * D
+    gen = np.random.Generator(np.random.PCG64(seed))
+    x = gen.standard_normal((B, N, E), dtype=np.float32)
+    w_qkv = gen.standard_normal((E, 3 * E), dtype=np.float32) * np.float32(1.0 / np.sqrt(E))
+    w_o = gen.standard_normal((E, E), dtype=np.float32) * np.float32(1.0 / np.sqrt(E))
+    dy = gen.standard_normal((B, N, E), dtype=np.float32)
+    out = [x, w_qkv, w_o, dy]
+    if dtype == "bf16":
+        out = [round_to_bf16(t) for t in out]
+    return out

@@ -227,3 +227,17 @@ def test_pair_count_varlen_matches_oracle(causal):
     N = 1024
     want = oracle.pair_count(len(lens), N, 3, pats, causal, lengths=[min(x, N) for x in lens])
     assert dla.pair_count_varlen(pats, causal, lens, N, 3) == want
+
+
+def test_layer_plan_check_sizes_and_errors():
+    pats = ((2048, 1), (4096, 2))
+    M, E = 2 * 4096, 768
+    ws_f, ws_b = dla.layer_plan_check(pats, True, 0.125, 2, 4096, 12)
+    attn_f, attn_b = dla.plan_check(pats, True, 0.125, 2, 4096, 12)
+    # forward: attention workspace + GEMM workspace; backward holds dA, dQKV, fp32 dX besides
+    assert ws_f >= attn_f and ws_b >= attn_b + M * E * (2 + 6 + 4)
+    with pytest.raises(dla.DlaError) as ei:
+        dla.layer_plan_check(pats, True, 0.125, 2, 4096, 0)
+    assert ei.value.code == dla.DLA_E_INVALID
+    with pytest.raises(dla.DlaError):
+        dla.layer_plan_check(((512, 3),), True, 0.125, 1, 1024, 12)
