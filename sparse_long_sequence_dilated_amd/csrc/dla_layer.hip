@@ -35,12 +35,20 @@ int check(const void* p, const char* name) {
     }                                                                                   \
   } while (0)
 
+// A strided batch of products: `count` problems, operand i at A + i sa,
+// B + i sb, C + i sc (strides in elements).
+struct Batch {
+  int count = 1;
+  int64_t sa = 0, sb = 0, sc = 0;
+};
+
 // Row-major C = op(A) op(B) + beta C, A and B bf16, C bf16 or fp32, fp32
 // accumulation.  A is [M, K] (or [K, M] with ta), B is [K, N] (or [N, K]),
 // C is [M, N]; lda, ldb, ldc are their row-major leading dimensions.
 int gemm_rm(hipblasLtHandle_t h, hipStream_t st, void* ws, size_t ws_bytes, bool ta, bool tb,
             int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-            int64_t ldb, void* C, int64_t ldc, hipDataType ctype, float beta) {
+            int64_t ldb, void* C, int64_t ldc, hipDataType ctype, float beta,
+            const Batch& bt = Batch{}) {
   int rc = DLA_OK;
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
@@ -58,6 +66,16 @@ int gemm_rm(hipblasLtHandle_t h, hipStream_t st, void* ws, size_t ws_bytes, bool
   DLA_BLAS(hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, tb ? K : N, tb ? N : K, ldb));
   DLA_BLAS(hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, ta ? M : K, ta ? K : M, lda));
   DLA_BLAS(hipblasLtMatrixLayoutCreate(&lc, ctype, N, M, ldc));
+  if (bt.count > 1) {
+    const hipblasLtMatrixLayout_t lay[3] = {la, lb, lc};
+    const int64_t stride[3] = {bt.sb, bt.sa, bt.sc};
+    for (int i = 0; i < 3; ++i) {
+      DLA_BLAS(hipblasLtMatrixLayoutSetAttribute(lay[i], HIPBLASLT_MATRIX_LAYOUT_BATCH_COUNT, &bt.count,
+                                                 sizeof(bt.count)));
+      DLA_BLAS(hipblasLtMatrixLayoutSetAttribute(lay[i], HIPBLASLT_MATRIX_LAYOUT_STRIDED_BATCH_OFFSET,
+                                                 &stride[i], sizeof(stride[i])));
+    }
+  }
   DLA_BLAS(hipblasLtMatmulPreferenceCreate(&pref));
   DLA_BLAS(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
                                                  &wsb, sizeof(wsb)));
@@ -97,6 +115,43 @@ hipError_t launch_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Weight gradients W^T-shaped [E, E] = X^T dP reduce over all M = B N rows.
+// One product of that shape has only (E / tile)^2 output tiles, too few to
+// fill the chip, so the rows are cut into `splits` chunks: a strided batch of
+// products writes one fp32 partial per chunk, and one pass sums them.
+int weight_splits(int64_t M) {
+  int s = 1;
+  while (s < 16 && M % (2 * s) == 0 && M / (2 * s) >= 2048) s *= 2;
+  return s;
+}
+
+// out[j] (row stride ldo[j]) = sum over s of part[j][s], for j < 4 gradients of [E, E].
+struct SplitSumArgs {
+  const float* part;  // [4, splits, E, E]
+  float* out[4];
+  int64_t ldo[4];
+  int splits;
+  int E;
+};
+
+__global__ __launch_bounds__(256) void split_sum_kernel(SplitSumArgs a) {
+  const int j = blockIdx.y;
+  const int64_t ee = (int64_t)a.E * a.E;
+  const float* base = a.part + (int64_t)j * a.splits * ee;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < ee; i += (int64_t)gridDim.x * 256 * 4) {
+    float4 acc = *(const float4*)(base + i);
+    for (int s = 1; s < a.splits; ++s) {
+      const float4 t = *(const float4*)(base + s * ee + i);
+      acc.x += t.x;
+      acc.y += t.y;
+      acc.z += t.z;
+      acc.w += t.w;
+    }
+    const int64_t row = i / a.E, col = i % a.E;  // E % 4 == 0: a float4 stays in one row
+    *(float4*)(a.out[j] + row * a.ldo[j] + col) = acc;
+  }
+}
+
 // q, k, v, the attention output and the gradients: contiguous [B, N, H, D].
 dla_shape head_shape(int64_t B, int64_t N, int64_t H) {
   dla_shape s{};
@@ -112,8 +167,9 @@ dla_shape head_shape(int64_t B, int64_t N, int64_t H) {
 }
 
 // Layer workspace: forward = attention workspace + GEMM workspace; backward
-// = dA [M, E] bf16 + dQKV [3, M, E] bf16 + dX [M, E] fp32 + attention
-// backward workspace + GEMM workspace.
+// = dA [M, E] bf16 + dQKV [3, M, E] bf16 + dX [M, E] fp32 + weight-gradient
+// partials [4, splits, E, E] fp32 + attention backward workspace + GEMM
+// workspace.
 int layer_plan(const dla_desc* desc, int64_t B, int64_t N, int64_t H, size_t* fwd, size_t* bwd) {
   if (B < 1 || N < 1 || H < 1) return fail(DLA_E_INVALID, "B, N and H must be positive");
   dla_shape s = head_shape(B, N, H);
@@ -122,7 +178,10 @@ int layer_plan(const dla_desc* desc, int64_t B, int64_t N, int64_t H, size_t* fw
   if (rc) return rc;
   const size_t M = (size_t)B * N, E = (size_t)H * kD;
   if (fwd) *fwd = align256(af) + kGemmWs;
-  if (bwd) *bwd = align256(M * E * 2) + align256(M * 3 * E * 2) + align256(M * E * 4) + align256(ab) + kGemmWs;
+  const size_t parts = (size_t)4 * weight_splits((int64_t)M) * E * E * 4;
+  if (bwd)
+    *bwd = align256(M * E * 2) + align256(M * 3 * E * 2) + align256(M * E * 4) + align256(parts) + align256(ab) +
+           kGemmWs;
   return DLA_OK;
 }
 
@@ -205,13 +264,18 @@ extern "C" int dla_layer_backward(const dla_desc* desc, int64_t B, int64_t N, in
   char* da = (char*)ws;                                         // dA [M, E] bf16
   char* dqkv = da + align256((size_t)M * E * 2);                // dQ, dK, dV [3, M, E] bf16
   char* dxf = dqkv + align256((size_t)M * 3 * E * 2);           // dX [M, E] fp32
-  char* aws = dxf + align256((size_t)M * E * 4);                // attention backward workspace
+  const int S = weight_splits(M);
+  float* part = (float*)(dxf + align256((size_t)M * E * 4));    // [4, S, E, E] fp32
+  char* aws = (char*)part + align256((size_t)4 * S * E * E * 4);  // attention backward workspace
   const size_t aws_bytes = need - kGemmWs - (size_t)(aws - (char*)ws);
   char* gws = (char*)ws + (need - kGemmWs);
-  // dA = dY W_o^T, dW_o = A^T dY
+  // dA = dY W_o^T; partials of dW_o = A^T dY (chunk s: rows s M / S ...)
+  const int64_t mk = M / S;
+  const Batch wb{S, mk * E, mk * E, E * E};
   if ((rc = gemm_rm(h, st, gws, kGemmWs, false, true, M, E, E, dy, E, w_o, E, da, E, HIP_R_16BF, 0.f)))
     return rc;
-  if ((rc = gemm_rm(h, st, gws, kGemmWs, true, false, E, E, M, attn, E, dy, E, dw_o, E, HIP_R_32F, 0.f)))
+  if ((rc = gemm_rm(h, st, gws, kGemmWs, true, false, E, E, mk, attn, E, dy, E, part + 3 * S * E * E, E,
+                    HIP_R_32F, 0.f, wb)))
     return rc;
   // dQ, dK, dV
   const dla_shape s = head_shape(B, N, H);
@@ -228,8 +292,23 @@ extern "C" int dla_layer_backward(const dla_desc* desc, int64_t B, int64_t N, in
   hipError_t e = launch_f32_to_bf16((const float*)dxf, dx, M * E, st);
   if (e != hipSuccess) return fail(DLA_E_HIP, "conversion launch: %s", hipGetErrorString(e));
   for (int j = 0; j < 3; ++j)
-    if ((rc = gemm_rm(h, st, gws, kGemmWs, true, false, E, E, M, x, E, dqkv + j * t, E, dw_qkv + j * E,
-                      3 * E, HIP_R_32F, 0.f)))
+    if ((rc = gemm_rm(h, st, gws, kGemmWs, true, false, E, E, mk, x, E, dqkv + j * t, E, part + j * S * E * E,
+                      E, HIP_R_32F, 0.f, wb)))
       return rc;
+  // dW_qkv column blocks and dW_o: sums of the partials
+  SplitSumArgs sa{};
+  sa.part = part;
+  for (int j = 0; j < 3; ++j) {
+    sa.out[j] = dw_qkv + j * E;
+    sa.ldo[j] = 3 * E;
+  }
+  sa.out[3] = dw_o;
+  sa.ldo[3] = E;
+  sa.splits = S;
+  sa.E = (int)E;
+  const int64_t blocks = std::min<int64_t>((E * E / 4 + 255) / 256, 1024);
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)blocks, 4), dim3(256), 0, st, sa);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(DLA_E_HIP, "split sum launch: %s", hipGetErrorString(e));
   return DLA_OK;
 }

@@ -6,7 +6,8 @@ model settings of the gptget.net summary of arXiv 2307.02486 (section
 through the C ABI (hipBLASLt projections, the library's attention); the
 results are compared with the fp64 layer oracle on the same bf16 inputs.
 At the 32K-token size the oracle evaluates sampled rows of Y one by one, and
-dW_o is checked against A^T dY in fp64 from the layer's own A.
+dW_o (summed from 16 row chunks) is checked against A^T dY in fp64 from the
+layer's own A.
 """
 import zlib
 
@@ -26,7 +27,8 @@ CASES = [
     # (B, N, patterns, causal)
     (2, 1024, ((256, 1), (512, 2), (1024, 4)), True),
     (1, 1000, ((512, 1), (1024, 2)), False),                    # cut-short segments
-    (1, 2048, inputs.geometric_patterns(2048, 2, 5), True),     # 2K sequence, 32K pattern set
+    (4, 2048, inputs.geometric_patterns(2048, 2, 5), True),     # 2K sequences, 32K pattern set;
+                                                                # weight gradients in 4 row chunks
 ]
 
 
