@@ -309,6 +309,8 @@ def main():
     ap.add_argument("--workload", default="C5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-forward-lines", action="store_true")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="only run the attention-layer legs (for profiling them)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -329,6 +331,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+
+    if args.layer_only:
+        print(json.dumps({"layer": [layer_bench(16, 2048, args.steps, args.warmup),
+                                    layer_bench(1, 32768, args.steps, args.warmup)]}), flush=True)
         return
 
     wl = inputs.WORKLOADS[args.workload]
