@@ -141,6 +141,41 @@ int dla_backward_varlen(const dla_desc* desc, const dla_shape* shape, const int3
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---- 8-bit keys and values ([G] 方法详解, last item: quantization combines
+ * with the method) ----
+ *
+ * K and V are stored as FP8 E4M3 codes (the OCP 8-bit format: bias 7,
+ * largest finite value 448, no infinities) with one fp32 scale per
+ * (batch, head); the attention reads K = code * k_scale[b * H + h], and V
+ * likewise.  Codes use the element strides of the bf16 shape, one byte per
+ * element; scales are [B, H] fp32, 4-byte aligned.
+ *
+ * dla_quantize_fp8: codes and scales of a bf16 tensor x (shape->dtype =
+ * DLA_BF16, D = 64).  Per head, amax = max |x| over its N rows and 64
+ * columns; inv = 448 / amax and scale = amax / 448, both rounded to fp32
+ * (inv = scale = 1 for an all-zero head); code = the E4M3 value nearest to
+ * fp32(x * inv), ties to even, after clamping to +-448.  x8 is device memory
+ * the caller owns; scale is written last (it holds the amaxes while the call
+ * runs).  B * H <= 65535.  Asynchronous on `stream`; nothing is allocated.
+ * Errors: DLA_E_INVALID (null or misaligned pointer, bad strides),
+ * DLA_E_UNSUPPORTED (dtype, D, B * H), DLA_E_HIP.
+ */
+int dla_quantize_fp8(const dla_shape* shape, const void* x, uint8_t* x8, float* scale, void* stream);
+
+/*
+ * dla_forward with 8-bit keys and values: q, o, lse as for dla_forward
+ * (shape->dtype must be DLA_BF16), k8/v8 codes and k_scale/v_scale scales as
+ * above.  The same workspace as dla_forward (dla_plan_check).  The codes are
+ * decoded exactly to bf16 inside the kernel; the rest of the arithmetic is
+ * dla_forward's.
+ * Errors: as dla_forward; DLA_E_UNSUPPORTED for an fp32 shape.
+ */
+int dla_forward_fp8kv(const dla_desc* desc, const dla_shape* shape, const void* q,
+                      const uint8_t* k8, const uint8_t* v8, const float* k_scale,
+                      const float* v_scale, void* o, float* lse, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
  * dla_pair_count for batches of different lengths; here lengths is host
  * memory (B entries, clamped to [0, N]).  Host only.
  * Errors: DLA_E_INVALID, DLA_E_UNSUPPORTED.

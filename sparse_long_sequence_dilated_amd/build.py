@@ -31,7 +31,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 HOST_SOURCES = ["dla_plan.cpp"]
 HIP_SOURCES = ["dla_api.hip", "dla_bwd_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
                "combine.hip", "attn_bwd_bf16.hip", "bwd_misc.hip", "dla_timing.hip",
-               "shard.hip", "dla_layer.hip"]
+               "shard.hip", "dla_layer.hip", "quant.hip"]
 LINK_FLAGS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 

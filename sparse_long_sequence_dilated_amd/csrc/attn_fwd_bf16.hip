@@ -36,6 +36,16 @@
 // then the true row maximum is taken, P recomputed, and the rescale of O and
 // l is applied before O's next update.  Row sums add the bf16-rounded P that
 // feeds the MFMA (v_dot2c_f32_bf16).
+//
+// 8-bit keys and values (the quantization the gptget.net page, section
+// 方法详解, pairs with the method): K and V arrive as FP8 E4M3 codes with one
+// scale per (batch, head).  Every E4M3 value is exact in bf16, so the tiles
+// are decoded to bf16 on their way into the same LDS ring and the MFMA loop
+// is unchanged; the key scale folds into the softmax constant and the value
+// scale into the epilogue.  The codes take a register detour (global load,
+// v_cvt_scalef32_pk_bf16_fp8, ds_write) instead of the DMA: each lane loads
+// 8 codes of a tile one window ahead and writes their bf16 image after the
+// next barrier, into the stage the DMA would have filled.
 #include "dla_device.h"
 
 namespace dla {
@@ -49,6 +59,7 @@ constexpr float kSumLimit = 65536.f;
 // 11:8).  Issued through the builtin, not inline asm, so that the compiler's
 // own wait insertion sees them and knows which loads have completed.
 constexpr int kVmcnt0 = 0x0F70;
+constexpr int kLgkmcnt0 = 0xC07F;  // LDS (and scalar) operations only
 
 struct __align__(16) FwdStage {
   uint4 k[kFwdBN * 8];  // 8 KB
@@ -56,9 +67,11 @@ struct __align__(16) FwdStage {
 };
 
 // kShard: some pattern reads gathered keys (a sequence shard); the plain
-// instantiation has none of that logic.
-template <bool kShard>
+// instantiation has none of that logic.  kFp8: keys and values are E4M3
+// codes (never together with kShard).
+template <bool kShard, bool kFp8>
 __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs a) {
+  static_assert(!(kShard && kFp8), "sequence shards read bf16 keys");
   __shared__ FwdStage ring[kStages];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -97,7 +110,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   const bool wave_active = qw0 < L;
   const int wave_kend = a.causal ? min(Lk, qgw0 + 32) : Lk;
   const int nh = wave_active ? (wave_kend + 31) / 32 : 0;  // half tiles this wave computes
-  const float c = a.scale_log2;
+  const float c = kFp8 ? a.scale_log2 * a.k_scale[(int64_t)b * a.H + h] : a.scale_log2;
 
   // Q as the B operand: lane (query li, group lg) holds d = 16*ks + 8*lg .. +8.
   bf16x8 qop[4];
@@ -129,8 +142,9 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   const int tiles_per_chunk = ext ? (int)(cr / kFwdBN) : 0x7FFFFFFF;
   const int64_t chunk_jump = ext ? ((int64_t)a.B * a.H - 1) * cr * kD * 2 : 0;
   int tc = 0;
-  const char* kcur = (const char*)Kh;
-  const char* vcur = (const char*)Vh;
+  // (With kFp8, Kh and Vh are byte pointers in the same element units.)
+  const char* kcur = kFp8 ? (const char*)a.k + head_off + base_row * a.sn : (const char*)Kh;
+  const char* vcur = kFp8 ? (const char*)a.v + head_off + base_row * a.sn : (const char*)Vh;
   auto issue_tile = [&](int kt, FwdStage* __restrict__ dst) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kcur, span);
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vcur, span);
@@ -144,6 +158,35 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
     const uint32_t o = kt == tail_kt ? otail : doff;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst->k + 8 * (8 * wave)), 16, o, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst->v + 8 * (8 * wave)), 16, o, 0, 0, 0);
+  };
+
+  // ---- 8-bit keys and values: lane l of wave w loads the 8 codes of the
+  // logical chunk that belongs at LDS slot l % 8 of row 8w + l / 8 (the
+  // DMA's placement), tiles one window ahead into stk/stv, and writes their
+  // bf16 image to that slot: byte 16 * tid of the stage's K or V tile.
+  const uint32_t cchunk8 = 8u * (uint32_t)((lane & 7) ^ u_swz(dma_row));
+  const uint32_t doff8 = (uint32_t)dma_row * (uint32_t)kstride + cchunk8;
+  const uint32_t otail8 = (uint32_t)min(dma_row, Lk - 1 - tail_kt * kFwdBN) * (uint32_t)kstride + cchunk8;
+  const int64_t tile_bytes8 = (int64_t)kFwdBN * kstride;
+  uint2 stk[2], stv[2];
+  auto load_tile8 = [&](int kt, int slot) __attribute__((always_inline)) {
+    const uint32_t o = kt == tail_kt ? otail8 : doff8;
+    stk[slot] = *(const uint2*)(kcur + o);
+    stv[slot] = *(const uint2*)(vcur + o);
+    kcur += tile_bytes8;
+    vcur += tile_bytes8;
+  };
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
+  auto decode8 = [](uint2 x) __attribute__((always_inline)) {
+    return u32x4v{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true))};
+  };
+  auto store_tile8 = [&](int slot, FwdStage* __restrict__ dst) __attribute__((always_inline)) {
+    *(lds_u32x4*)((lds_char*)(lds_u4*)dst->k + 16 * tid) = decode8(stk[slot]);
+    *(lds_u32x4*)((lds_char*)(lds_u4*)dst->v + 16 * tid) = decode8(stv[slot]);
   };
 
   // ---- per-lane LDS operand offsets -------------------------------------------
@@ -291,17 +334,27 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   // for.  Tile t lives in stage t % 5; the distinct restrict pointers tell
   // the compiler that the DMA targets are not read in the window, so it adds
   // no waits of its own.
+  // With kFp8 the window writes the bf16 images of tiles j+3 and j+4 (loaded
+  // into registers one window earlier) to those stages and loads tiles j+5
+  // and j+6; the barrier then waits for the LDS writes instead of the DMA.
   auto window = [&](int j, const FwdStage* __restrict__ s0, const FwdStage* __restrict__ s1,
                     const FwdStage* __restrict__ s2, FwdStage* __restrict__ i3,
                     FwdStage* __restrict__ i4) __attribute__((always_inline)) {
     if (j > 0) {
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __builtin_amdgcn_s_waitcnt(kFp8 ? kLgkmcnt0 : kVmcnt0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
-    if (j + 3 < nkt) issue_tile(j + 3, i3);
-    if (j + 4 < nkt) issue_tile(j + 4, i4);
+    if constexpr (kFp8) {
+      if (j + 3 < nkt) store_tile8(0, i3);
+      if (j + 4 < nkt) store_tile8(1, i4);
+      if (j + 5 < nkt) load_tile8(j + 5, 0);
+      if (j + 6 < nkt) load_tile8(j + 6, 1);
+    } else {
+      if (j + 3 < nkt) issue_tile(j + 3, i3);
+      if (j + 4 < nkt) issue_tile(j + 4, i4);
+    }
     if (2 * j + 1 < nh) phase(2 * j + 1, 1, s0, s1, pa, pb);
     if (2 * j + 2 < nh) phase(2 * j + 2, 0, s0, s1, pb, pa);
     if (2 * j + 3 < nh) phase(2 * j + 3, 1, s1, s2, pa, pb);
@@ -310,11 +363,25 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
 
   // Prologue: tiles 0..2 in LDS (the first window reads all three; stages 3
   // and 4 are still unused, so B_0 needs no barrier), S and P of half tile 0.
-  issue_tile(0, &ring[0]);
-  if (nkt > 1) issue_tile(1, &ring[1]);
-  if (nkt > 2) issue_tile(2, &ring[2]);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      asm volatile("" ::: "memory");
+  if constexpr (kFp8) {
+    load_tile8(0, 0);
+    if (nkt > 1) load_tile8(1, 1);
+    store_tile8(0, &ring[0]);
+    if (nkt > 1) store_tile8(1, &ring[1]);
+    if (nkt > 2) {
+      load_tile8(2, 0);
+      store_tile8(0, &ring[2]);
+    }
+    if (nkt > 3) load_tile8(3, 0);
+    if (nkt > 4) load_tile8(4, 1);
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+  } else {
+    issue_tile(0, &ring[0]);
+    if (nkt > 1) issue_tile(1, &ring[1]);
+    if (nkt > 2) issue_tile(2, &ring[2]);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  }
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   if (nh > 0) {
@@ -352,7 +419,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   const float lt = xhalf_sum(l_run);
   const int row = qw0 + li;
   if (row >= L) return;
-  const float inv = 1.f / lt;
+  const float inv = (kFp8 ? a.v_scale[bh] : 1.f) / lt;
   const float lse = (m_run + __builtin_amdgcn_logf(lt)) * kLn2;
   __bf16* dst;
   float* lse_dst;
@@ -382,13 +449,20 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream) {
   if (a.sched.total == 0) return hipSuccess;
   bool shard = false;
   for (int i = 0; i < a.P; ++i) shard |= a.ext_k[i] != nullptr;
+  if (shard && a.k_scale) return hipErrorInvalidValue;  // not built: the planner rejects it first
+  if (a.k_scale) {
+    TimedLaunch tl("attn_fwd_fp8", stream);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, true>), dim3((unsigned)a.sched.total),
+                       dim3(64 * kFwdWaves), 0, stream, a);
+    return hipGetLastError();
+  }
   TimedLaunch tl("attn_fwd", stream);
   if (shard)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)a.sched.total), dim3(64 * kFwdWaves),
-                       0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<true, false>), dim3((unsigned)a.sched.total),
+                       dim3(64 * kFwdWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)a.sched.total), dim3(64 * kFwdWaves),
-                       0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, false>), dim3((unsigned)a.sched.total),
+                       dim3(64 * kFwdWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -45,7 +45,8 @@ static void fill_fwd_args(const Plan& pl, AttnFwdArgs* a) {
 // Attention pass and merge for a validated plan (whole sequence or shard).
 static int forward_impl(const Plan& pl, const void* q, const void* k, const void* v,
                         const void* const* ext_k, const void* const* ext_v, void* o, float* lse,
-                        void* ws, size_t ws_bytes, void* stream, const int32_t* lengths = nullptr) {
+                        void* ws, size_t ws_bytes, void* stream, const int32_t* lengths = nullptr,
+                        const float* k_scale = nullptr, const float* v_scale = nullptr) {
   int rc;
   if (pl.empty) return DLA_OK;  // nothing is read or written; pointers may be null
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
@@ -62,6 +63,8 @@ static int forward_impl(const Plan& pl, const void* q, const void* k, const void
   a.o = o;
   a.lse = lse;
   a.lengths = lengths;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   fill_fwd_args(pl, &a);
   for (int i = 0; i < pl.P; ++i) {
     if (!pl.span[i]) continue;
@@ -157,6 +160,58 @@ extern "C" int dla_forward_varlen(const dla_desc* desc, const dla_shape* shape,
   if (!pl.empty && (!lengths || ((uintptr_t)lengths & 3u)))
     return fail(DLA_E_INVALID, "lengths is null or not 4-byte aligned");
   return forward_impl(pl, q, k, v, nullptr, nullptr, o, lse, ws, ws_bytes, stream, lengths);
+}
+
+static int check_f32(const void* p, const char* name) {
+  if (!p) return fail(DLA_E_INVALID, "%s is null", name);
+  if ((uintptr_t)p & 3u) return fail(DLA_E_INVALID, "%s is not 4-byte aligned", name);
+  return DLA_OK;
+}
+
+extern "C" int dla_forward_fp8kv(const dla_desc* desc, const dla_shape* shape, const void* q,
+                                 const uint8_t* k8, const uint8_t* v8, const float* k_scale,
+                                 const float* v_scale, void* o, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  clear_error();
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl);
+  if (rc) return rc;
+  if (pl.dtype != DLA_BF16) return fail(DLA_E_UNSUPPORTED, "8-bit keys and values need bf16 q and o");
+  if (pl.empty) return DLA_OK;
+  if ((rc = check_f32(k_scale, "k_scale")) || (rc = check_f32(v_scale, "v_scale"))) return rc;
+  return forward_impl(pl, q, k8, v8, nullptr, nullptr, o, lse, ws, ws_bytes, stream, nullptr, k_scale,
+                      v_scale);
+}
+
+extern "C" int dla_quantize_fp8(const dla_shape* shape, const void* x, uint8_t* x8, float* scale,
+                                void* stream) {
+  clear_error();
+  if (!shape) return fail(DLA_E_INVALID, "null shape");
+  if (shape->dtype != DLA_BF16) return fail(DLA_E_UNSUPPORTED, "quantization reads bf16");
+  if (shape->D != kD) return fail(DLA_E_UNSUPPORTED, "head dimension must be %d", kD);
+  if (shape->B < 0 || shape->N < 0 || shape->H < 0) return fail(DLA_E_INVALID, "negative size");
+  if (shape->stride_b <= 0 || shape->stride_n <= 0 || shape->stride_h <= 0)
+    return fail(DLA_E_INVALID, "strides must be positive");
+  if (shape->stride_b % 8 || shape->stride_n % 8 || shape->stride_h % 8)
+    return fail(DLA_E_INVALID, "strides must be multiples of 8 elements");
+  if (shape->B * shape->H > 65535) return fail(DLA_E_UNSUPPORTED, "B * H exceeds 65535");
+  if (shape->B * shape->H == 0) return DLA_OK;
+  int rc;
+  if ((rc = check_f32(scale, "scale"))) return rc;
+  if (shape->N > 0 && ((rc = check_ptr(x, "x")) || (rc = check_ptr(x8, "x8")))) return rc;
+  QuantArgs a{};
+  a.x = x;
+  a.x8 = x8;
+  a.scale = scale;
+  a.sb = shape->stride_b;
+  a.sn = shape->stride_n;
+  a.sh = shape->stride_h;
+  a.B = shape->B;
+  a.N = shape->N;
+  a.H = shape->H;
+  hipError_t e = launch_quantize_fp8(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantization launch");
+  return DLA_OK;
 }
 
 extern "C" int dla_forward_shard(const dla_desc* desc, const dla_shape* shape,

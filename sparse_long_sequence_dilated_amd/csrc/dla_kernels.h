@@ -36,6 +36,11 @@ struct AttnFwdArgs {
   const void* ext_v[kMaxP];
   Schedule sched;
   const int32_t* lengths;  // per-batch sequence lengths (device), null: all N
+  // 8-bit keys and values: k and v hold FP8 E4M3 codes (same element
+  // strides, one byte each) and the head's K is code * k_scale[b * H + h],
+  // likewise V.  Null for bf16 keys and values.
+  const float* k_scale;
+  const float* v_scale;
 };
 
 // Merge of the per-pattern results into o/lse.
@@ -184,6 +189,16 @@ class TimedLaunch {
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a, hipStream_t stream);
+
+// Per-(batch, head) FP8 E4M3 quantization of a bf16 [B, N, H, D] tensor.
+struct QuantArgs {
+  const void* x;   // bf16
+  uint8_t* x8;     // codes, same element strides
+  float* scale;    // [B, H]: the head's amax (as bits) while the pass runs, then the scale
+  int64_t sb, sn, sh;
+  int64_t B, N, H;
+};
+hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_shard_gather(const ShardGatherArgs& a, hipStream_t stream);
 hipError_t launch_pad_rows(const CombineArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_shard_ld(const ShardLdArgs& a, hipStream_t stream);

@@ -28,7 +28,7 @@ EXPORTS = ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_
            "dla_plan_check_shard", "dla_pair_count_shard", "dla_shard_gather", "dla_forward_shard",
            "dla_backward_shard", "dla_shard_finish", "dla_forward_varlen", "dla_backward_varlen",
            "dla_pair_count_varlen", "dla_blas_create", "dla_blas_destroy", "dla_layer_plan_check",
-           "dla_layer_forward", "dla_layer_backward",
+           "dla_layer_forward", "dla_layer_backward", "dla_quantize_fp8", "dla_forward_fp8kv",
            "dla_timing_enable", "dla_timing_collect", "dla_strerror", "dla_last_error")
 
 
@@ -89,6 +89,8 @@ def lib():
     L.dla_forward_varlen.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dla_backward_varlen.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dla_pair_count_varlen.argtypes = [pd, ps, ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    L.dla_quantize_fp8.argtypes = [ps, vp, vp, vp, vp]
+    L.dla_forward_fp8kv.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dla_blas_create.argtypes = [ctypes.POINTER(vp)]
     L.dla_blas_destroy.argtypes = [vp]
     L.dla_layer_plan_check.argtypes = [pd, i64, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
@@ -109,7 +111,7 @@ def lib():
                  "dla_forward_shard", "dla_backward_shard", "dla_shard_finish",
                  "dla_forward_varlen", "dla_backward_varlen", "dla_pair_count_varlen",
                  "dla_blas_create", "dla_blas_destroy", "dla_layer_plan_check", "dla_layer_forward",
-                 "dla_layer_backward"):
+                 "dla_layer_backward", "dla_quantize_fp8", "dla_forward_fp8kv"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -571,3 +573,48 @@ def layer_backward(x, w_qkv, w_o, qkv, attn, lse, dy, patterns, blas, causal=Tru
                                     dw_o.data_ptr(), blas.handle, workspace.data_ptr(),
                                     workspace.numel(), _stream(stream, x.device)))
     return dx, dw_qkv, dw_o
+
+
+# ---- 8-bit keys and values ----
+
+def quantize_fp8(x, stream=None):
+    """FP8 E4M3 codes of a bf16 [B, N, H, 64] tensor and its per-(batch, head)
+    fp32 scales: returns (codes uint8 with x's layout, scale [B, H])."""
+    import torch
+    if x.dtype != torch.bfloat16:
+        raise DlaError(DLA_E_UNSUPPORTED, "quantization reads bfloat16")
+    shape = _shape_of(x)
+    B, N, H, _ = x.shape
+    x8 = torch.empty_strided(x.shape, x.stride(), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    _check(lib().dla_quantize_fp8(ctypes.byref(shape), x.data_ptr(), x8.data_ptr(), scale.data_ptr(),
+                                  _stream(stream, x.device)))
+    return x8, scale
+
+
+def forward_fp8kv(q, k8, v8, k_scale, v_scale, patterns, causal=True, scale=None, out=None, lse=None,
+                  workspace=None, stream=None):
+    """dla forward with FP8 E4M3 keys and values (codes with q's layout, [B, H] scales)."""
+    import torch
+    scale = default_scale(q.shape[-1]) if scale is None else scale
+    for t in (k8, v8):
+        if t.shape != q.shape or t.stride() != q.stride() or t.dtype != torch.uint8 or t.device != q.device:
+            raise DlaError(DLA_E_INVALID, "k8 and v8 must be uint8 tensors with q's shape and strides")
+    B, N, H, _ = q.shape
+    for t in (k_scale, v_scale):
+        if tuple(t.shape) != (B, H) or not t.is_contiguous() or t.dtype != torch.float32:
+            raise DlaError(DLA_E_INVALID, "scales must be contiguous float32 [B, H] tensors")
+    shape = _shape_of(q)
+    desc = make_desc(patterns, causal, scale)
+    ws_f = ctypes.c_size_t(0)
+    _check(lib().dla_plan_check(ctypes.byref(desc), ctypes.byref(shape), ctypes.byref(ws_f), None))
+    o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
+    _same_layout(q, o)
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        workspace = torch.empty(max(ws_f.value, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().dla_forward_fp8kv(ctypes.byref(desc), ctypes.byref(shape), q.data_ptr(), k8.data_ptr(),
+                                   v8.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(),
+                                   lse_t.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   _stream(stream, q.device)))
+    return o, lse_t
