@@ -7,6 +7,8 @@
 // slots, the amax pass (one vector atomic max per wave on the float bits,
 // which order like unsigned integers for non-negative values), the
 // quantization pass, and amax -> scale.
+#include <algorithm>
+
 #include "dla_device.h"
 #include "dla_kernels.h"
 
@@ -32,19 +34,27 @@ __device__ __forceinline__ float amax8(uint4 u) {
   return m;
 }
 
-// grid (ceil(N / 256), B * H)
+// grid (min(ceil(N / 256), kAmaxBlocks), B * H).  The heads' slots share a
+// cache line, where atomics serialise, so each workgroup strides over row
+// blocks and issues one atomic.
+constexpr int kAmaxBlocks = 64;
+
 __global__ __launch_bounds__(256) void q_amax_kernel(QuantArgs a) {
+  __shared__ float wmax[4];
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int sub = threadIdx.x & 7, rr = threadIdx.x >> 3;
   const __bf16* x = (const __bf16*)a.x + b * a.sb + h * a.sh + 8 * sub;
   float m = 0.f;
-  for (int i = 0; i < kQRows / 32; ++i) {
-    const int64_t n = (int64_t)blockIdx.x * kQRows + 32 * i + rr;
-    if (n < a.N) m = fmaxf(m, amax8(*(const uint4*)(x + n * a.sn)));
-  }
+  for (int64_t n = (int64_t)blockIdx.x * 32 + rr; n < a.N; n += (int64_t)gridDim.x * 32)
+    m = fmaxf(m, amax8(*(const uint4*)(x + n * a.sn)));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)(a.scale + bh), __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax((unsigned int*)(a.scale + bh), __float_as_uint(m));
+  }
 }
 
 __device__ __forceinline__ float inv_of(float amax) { return amax > 0.f ? __fdiv_rn(448.f, amax) : 1.f; }
@@ -93,8 +103,10 @@ hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t stream) {
   TimedLaunch tl("quantize_fp8", stream);
   hipLaunchKernelGGL(q_clear_kernel, small, dim3(256), 0, stream, a.scale, nbh);
   if (a.N > 0) {  // (an empty sequence keeps amax 0, so scale 1)
-    const dim3 grid((unsigned)((a.N + kQRows - 1) / kQRows), (unsigned)nbh);
-    hipLaunchKernelGGL(q_amax_kernel, grid, dim3(256), 0, stream, a);
+    const int64_t nblk = (a.N + kQRows - 1) / kQRows;
+    const dim3 grid((unsigned)nblk, (unsigned)nbh);
+    hipLaunchKernelGGL(q_amax_kernel, dim3((unsigned)std::min<int64_t>(nblk, kAmaxBlocks), (unsigned)nbh),
+                       dim3(256), 0, stream, a);
     hipLaunchKernelGGL(q_code_kernel, grid, dim3(256), 0, stream, a);
   }
   hipLaunchKernelGGL(q_scale_kernel, small, dim3(256), 0, stream, a.scale, nbh);
