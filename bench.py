@@ -14,6 +14,7 @@ Also reported, as extra fields of the same line:
     over 8 devices (the last shard, whose segments of the three coarsest
     patterns span 2, 4 and 8 devices): its exchange parts and its forward,
     and (`fwd_bwd`) forward plus backward, the collectives excluded;
+  * in `forward_only`, also the N=32768 forward with FP8 E4M3 keys and values;
   * `layer`: the attention layer around the operator (hipBLASLt projections,
     768 dimensions, 12 heads, random weights) at 16 x 2K and 1 x 32K tokens,
     forward and forward plus backward;
@@ -129,8 +130,8 @@ def time_steps(step, steps, warmup):
     t1 = time.perf_counter()
     dla.timing_enable(False)
     fams = {}
-    for fam in ("attn_fwd", "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd", "bwd_finalize",
-                "shard_gather", "shard_finish"):
+    for fam in ("attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "combine", "bwd_prep", "attn_bwd",
+                "bwd_finalize", "shard_gather", "shard_finish", "quantize_fp8"):
         n, ms = dla.timing_collect(fam)
         if n:
             fams[fam] = (n, ms)
@@ -158,6 +159,38 @@ def forward_only(name, steps, warmup):
     for fam, (n, fms) in fams.items():
         out[f"{fam}_us_per_launch"] = 1e3 * fms / n
     del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def fp8_forward(name, steps, warmup):
+    """Forward with FP8 E4M3 keys and values (quantized once, outside the
+    timed step, as a cache of keys and values would hold them)."""
+    import torch
+    from sparse_long_sequence_dilated_amd import dla, inputs
+    wl = inputs.WORKLOADS[name]
+    q, k, v = gpu_inputs(wl, 3, 1000 + wl.seed)
+    k8, ks = dla.quantize_fp8(k)
+    v8, vs = dla.quantize_fp8(v)
+    ws_f, _ = dla.plan_check(wl.patterns, wl.causal, wl.scale, wl.B, wl.N, wl.H)
+    ws = torch.empty(max(ws_f, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device="cuda")
+
+    def step():
+        dla.forward_fp8kv(q, k8, v8, ks, vs, wl.patterns, wl.causal, wl.scale, out=o, lse=lse,
+                          workspace=ws)
+
+    ms, fams = time_steps(step, steps, warmup)
+    qms, _ = time_steps(lambda: dla.quantize_fp8(k), steps, warmup)
+    pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
+    tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
+    out = {"workload": wl.describe() + ", keys and values FP8 E4M3 with per-head scales",
+           "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "ms": ms, "useful_tflops": tflops,
+           "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS, "quantize_one_tensor_ms": qms}
+    for fam, (n, fms) in fams.items():
+        out[f"{fam}_us_per_launch"] = 1e3 * fms / n
+    del q, k, v, k8, v8, ks, vs, o, lse, ws
     torch.cuda.empty_cache()
     return out
 
@@ -231,27 +264,31 @@ def shard_forward(name, devices, shard, steps, warmup):
     return out
 
 
-def cpu_baseline(wl, heads=4):
-    """The oracle (float32, thread pool) on batch 0 and `heads` heads of the workload."""
+def cpu_baseline(wl, min_seconds=10.0, max_passes=30):
+    """The oracle (float32, thread pool) on batch 0 of the workload, all heads,
+    repeated until about `min_seconds` of CPU work have run."""
     import numpy as np
 
     import oracle
     from sparse_long_sequence_dilated_amd import inputs
     workers = max(1, min(16, os.cpu_count() or 1))
-    q, k, v, do = inputs.draw((1, wl.N, heads, wl.D), wl.seed, 4, wl.dtype)
-    t0 = time.perf_counter()
-    o, lse = oracle.forward(q, k, v, wl.patterns, wl.causal, wl.scale, dtype=np.float32,
+    q, k, v, do = inputs.draw((1, wl.N, wl.H, wl.D), wl.seed, 4, wl.dtype)
+    passes, t = 0, 0.0
+    while passes < max_passes and (passes == 0 or t < min_seconds):
+        t0 = time.perf_counter()
+        o, lse = oracle.forward(q, k, v, wl.patterns, wl.causal, wl.scale, dtype=np.float32,
+                                workers=workers)
+        if wl.backward:
+            oracle.backward(q, k, v, o, lse, do, wl.patterns, wl.causal, wl.scale, dtype=np.float32,
                             workers=workers)
-    if wl.backward:
-        oracle.backward(q, k, v, o, lse, do, wl.patterns, wl.causal, wl.scale, dtype=np.float32,
-                        workers=workers)
-    t = time.perf_counter() - t0
-    scale = (wl.B * wl.H) / heads
-    return {"value": wl.B * wl.N / (t * scale), "unit": "tokens/s", "cores": workers,
+        t += time.perf_counter() - t0
+        passes += 1
+    per_pass = t / passes
+    return {"value": wl.B * wl.N / (per_pass * wl.B), "unit": "tokens/s", "cores": workers,
             "kind": "oracle",
-            "sample": (f"{'fwd+bwd' if wl.backward else 'fwd'} of batch 1 of {wl.B}, heads 0-{heads - 1} "
-                       f"of {wl.H}, full N={wl.N} and all patterns; float32 NumPy oracle, "
-                       f"{workers} threads, {t:.2f} s wall; scaled by {scale:g} to the full workload")}
+            "sample": (f"{'fwd+bwd' if wl.backward else 'fwd'} of batch 1 of {wl.B} (all {wl.H} heads, "
+                       f"full N={wl.N}, all patterns), {passes} passes in {t:.1f} s; float32 NumPy "
+                       f"oracle, {workers} threads; scaled by {wl.B} to the full batch")}
 
 
 def layer_bench(B, N, steps, warmup):
@@ -384,6 +421,7 @@ def main():
     if not args.no_forward_lines:
         extra.append(forward_only("C3", max(5, args.steps), args.warmup))
         extra.append(forward_only("C4", max(3, args.steps // 4), 1))
+        extra.append(fp8_forward("C3", max(5, args.steps), args.warmup))
         shard = shard_forward("C4", 8, 7, max(3, args.steps // 2), 1)
         layers = [layer_bench(16, 2048, max(5, args.steps // 2), 2),
                   layer_bench(1, 32768, max(5, args.steps // 2), 2)]
