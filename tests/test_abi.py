@@ -4,6 +4,7 @@ No compute call is made here (there is no GPU); dla_plan_check and
 dla_pair_count are host-only.  The planner is also rebuilt with g++ under
 the address and undefined-behaviour sanitizers and driven by a C harness.
 """
+import ctypes
 import os
 import re
 import subprocess
@@ -241,3 +242,23 @@ def test_layer_plan_check_sizes_and_errors():
     assert ei.value.code == dla.DLA_E_INVALID
     with pytest.raises(dla.DlaError):
         dla.layer_plan_check(((512, 3),), True, 0.125, 1, 1024, 12)
+
+
+def test_fp8_entry_points_reject_bad_arguments_before_any_launch():
+    L = dla.lib()
+    ok = dla.make_shape(1, 256, 2, 64, dla.DLA_BF16)
+    # quantization reads bf16 only, D = 64, strides multiple of 8, B * H <= 65535
+    for shape, code in ((dla.make_shape(1, 256, 2, 64, dla.DLA_F32), dla.DLA_E_UNSUPPORTED),
+                        (dla.make_shape(1, 256, 2, 32, dla.DLA_BF16, (256 * 2 * 32, 2 * 32, 32)),
+                         dla.DLA_E_UNSUPPORTED),
+                        (dla.make_shape(1, 256, 2, 64, dla.DLA_BF16, (256 * 132, 132, 66)), dla.DLA_E_INVALID),
+                        (dla.make_shape(300, 256, 300, 64, dla.DLA_BF16), dla.DLA_E_UNSUPPORTED)):
+        assert L.dla_quantize_fp8(ctypes.byref(shape), 16, 16, 16, None) == code
+    assert L.dla_quantize_fp8(ctypes.byref(ok), 16, 16, None, None) == dla.DLA_E_INVALID   # null scale
+    assert L.dla_quantize_fp8(ctypes.byref(ok), 16, 16, 18, None) == dla.DLA_E_INVALID     # misaligned scale
+    desc = dla.make_desc(((256, 1),), True, 0.125)
+    f32 = dla.make_shape(1, 256, 2, 64, dla.DLA_F32)
+    assert L.dla_forward_fp8kv(ctypes.byref(desc), ctypes.byref(f32), 16, 16, 16, 16, 16, 16, 16,
+                               16, 1 << 20, None) == dla.DLA_E_UNSUPPORTED
+    assert L.dla_forward_fp8kv(ctypes.byref(desc), ctypes.byref(ok), 16, 16, 16, None, 16, 16, 16,
+                               16, 1 << 20, None) == dla.DLA_E_INVALID
