@@ -43,8 +43,11 @@ constexpr int kBwdStages = 4;   // LDS ring depth (tiles in flight: 2)
 struct __align__(16) BwdStage {
   uint4 a[kBwdTile * 8];   // Q (key units) or K (query units): 64 rows x 128 B
   uint4 b[kBwdTile * 8];   // dO (key units) or V (query units)
-  float2 ld[kBwdTile];     // key units: (LSE * log2 e, D) of the tile's rows
+  // key units: -LSE * log2 e and -D of the tile's rows, in chunks of 16 rows:
+  // row i at 32 * (i / 16) + i % 16 and D 16 floats later
+  float ld[2 * kBwdTile];
 };
+
 
 // Number of patterns that keep row n of head h (n = h mod r for each).
 __device__ __forceinline__ int kept_count(const AttnBwdArgs& a, int n, int h) {
@@ -107,11 +110,11 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
       opb[ks] = bf16x8{};
     }
   }
-  float lse2_own = 0.f, d_own = 0.f;  // query units: this lane's query row
+  float nl2_own = 0.f, nd_own = 0.f;  // query units: -LSE * log2 e and -D of this lane's query
   if (!kKV && own < L) {
     const float2 x = ldh[(int64_t)own * r];
-    lse2_own = x.x;
-    d_own = x.y;
+    nl2_own = x.x;
+    nd_own = x.y;
   }
 
   // Streamed range: tiles t = 0..nt-1 start at row 64*(t_first + t); half h
@@ -152,7 +155,9 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     choff[i] = 16u * (uint32_t)((lane & 7) ^ u_swz(8 * i + (lane >> 3)));
     voff[i] = (uint32_t)(drow + 8 * i) * rsb + choff[i];
   }
-  const uint32_t ld_voff = (uint32_t)(16 * wave + (lane >> 1)) * (uint32_t)(8 * r) + 4u * (lane & 1);
+  // (-LSE2, -D) pairs of rows 16w .. 16w+15: lane l < 32 loads component
+  // l / 16 of row 16w + l % 16, so the tile holds the two as separate runs.
+  const uint32_t ld_voff = (uint32_t)(16 * wave + (lane & 15)) * (uint32_t)(8 * r) + 4u * ((lane >> 4) & 1);
   auto issue_tile = [&](int t, BwdStage* __restrict__ dst) __attribute__((always_inline)) {
     const int trow0 = kBwdTile * (t_first + t);
     const int lim = send - 1 - trow0;                   // last valid row of the tile
@@ -173,7 +178,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
       const __amdgpu_buffer_rsrc_t rl = buf_rsrc(ldh + (int64_t)trow0 * r, 63u * (uint32_t)(8 * r) + 8u);
       uint32_t lo = ld_voff;
       if (lim < kBwdTile - 1)
-        lo = (uint32_t)min(16 * wave + (lane >> 1), lim) * (uint32_t)(8 * r) + 4u * (lane & 1);
+        lo = (uint32_t)min(16 * wave + (lane & 15), lim) * (uint32_t)(8 * r) + 4u * ((lane >> 4) & 1);
       if (lane < 32)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)((float*)dst->ld + 32 * wave), 4, lo, 0, 0, 0);
     }
@@ -194,9 +199,25 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
 
   // ---- pipeline stages ------------------------------------------------------
   // S and dP of half hh (blk = hh & 1 within its tile).
+  // Key units start the dP accumulator at -D of each element's query, so
+  // that dS = P (dP - D) is one multiply.  (Element e = 4g + i of a lane is
+  // streamed row 32 blk + 8g + 4 lg + i.)
+  auto ld_offset = [&](int blk, int g) __attribute__((always_inline)) {
+    return 4 * (32 * (2 * blk + (g >> 1)) + 8 * (g & 1) + 4 * lg);  // bytes; D 64 bytes later
+  };
   auto stage_sd = [&](const BwdStage* __restrict__ st, int blk, f32x16& S, f32x16& P) __attribute__((always_inline)) {
     S = f32x16{};
-    P = f32x16{};
+    if (kKV) {
+      typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 nd = *(const lds_f32x4*)((const lds_char*)st->ld + ld_offset(blk, g) + 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P[4 * g + i] = nd[i];
+      }
+    } else {
+      P = f32x16{};
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 xa = lds_read_b128((const lds_u4*)st->a, blk * 4096 + roff[ks]);
@@ -211,24 +232,21 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     const int s0 = kBwdTile * t_first + 32 * hh;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      float l2[4], dd[4];
+      float nl[4];
       if (kKV) {
-        // rows 32*blk + 8g + 4lg + i of the tile: four (LSE2, D) pairs
         typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-        const lds_char* base = (const lds_char*)st->ld + 8 * (32 * blk + 8 * g + 4 * lg);
-        const f32x4 x0 = *(const lds_f32x4*)base;
-        const f32x4 x1 = *(const lds_f32x4*)(base + 16);
-        l2[0] = x0[0]; dd[0] = x0[1]; l2[1] = x0[2]; dd[1] = x0[3];
-        l2[2] = x1[0]; dd[2] = x1[1]; l2[3] = x1[2]; dd[3] = x1[3];
+        const f32x4 x = *(const lds_f32x4*)((const lds_char*)st->ld + ld_offset(blk, g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nl[i] = x[i];
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { l2[i] = lse2_own; dd[i] = d_own; }
+        for (int i = 0; i < 4; ++i) nl[i] = nl2_own;
       }
       float pv[4], dv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * g + i;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, -l2[i]));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, nl[i]));
         if (masked) {
           const int srow = s0 + 8 * g + 4 * lg + i;
           const bool dead = kKV ? (srow >= send || own >= L || (a.causal && own > srow))
@@ -236,7 +254,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
           if (dead) p = 0.f;
         }
         pv[i] = p;
-        dv[i] = p * (P[e] - dd[i]);
+        dv[i] = kKV ? p * P[e] : p * (P[e] + nd_own);
       }
       if (kKV) {
         pw[2 * g] = pack_bf16(pv[0], pv[1]);
@@ -276,24 +294,22 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   // VALU chunk g (elements 4g .. 4g+3) of stage_valu with no mask.
   auto valu_chunk = [&](const BwdStage* __restrict__ st, int blk, int g, const f32x16& S,
                         const f32x16& P, uint32_t (&pw)[8], uint32_t (&sw)[8]) __attribute__((always_inline)) {
-    float l2[4], dd[4];
+    float nl[4];
     if (kKV) {
       typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-      const lds_char* base = (const lds_char*)st->ld + 8 * (32 * blk + 8 * g + 4 * lg);
-      const f32x4 x0 = *(const lds_f32x4*)base;
-      const f32x4 x1 = *(const lds_f32x4*)(base + 16);
-      l2[0] = x0[0]; dd[0] = x0[1]; l2[1] = x0[2]; dd[1] = x0[3];
-      l2[2] = x1[0]; dd[2] = x1[1]; l2[3] = x1[2]; dd[3] = x1[3];
+      const f32x4 x = *(const lds_f32x4*)((const lds_char*)st->ld + ld_offset(blk, g));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nl[i] = x[i];
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { l2[i] = lse2_own; dd[i] = d_own; }
+      for (int i = 0; i < 4; ++i) nl[i] = nl2_own;
     }
     float pv[4], dv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * g + i;
-      pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, -l2[i]));
-      dv[i] = pv[i] * (P[e] - dd[i]);
+      pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, nl[i]));
+      dv[i] = kKV ? pv[i] * P[e] : pv[i] * (P[e] + nd_own);
     }
     if (kKV) {
       pw[2 * g] = pack_bf16(pv[0], pv[1]);

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdPrepArgs a) {
   s += __shfl_xor(s, 4);
   if (c == 0) {
     const int64_t i = (b * a.H + h) * a.N + n;
-    a.ld[i] = float2{a.lse[i] * kLog2e, s};
+    a.ld[i] = float2{-(a.lse[i] * kLog2e), -s};
   }
   const bool pad = n >= batch_len(a.lengths, b, a.N);  // past this batch's length
   if (a.zero_uncovered || pad) {

@@ -74,7 +74,7 @@ struct ShardGatherArgs {
 };
 
 struct ShardLdArgs {
-  const float2* ld;        // [B, H, N] (LSE * log2 e, D) pairs
+  const float2* ld;        // [B, H, N] (-LSE * log2 e, -D) pairs
   float2* out;             // [B, H, out_rows]
   int64_t B, H, N, r, cr, out_rows, out_row0;
 };
@@ -115,7 +115,7 @@ struct AttnBwdArgs {
   const void* k;
   const void* v;
   const void* dout;
-  const float2* ld;        // (combined LSE * log2 e, D = rowsum(dO*O)) [B,H,N]
+  const float2* ld;        // (-combined LSE * log2 e, -D), D = rowsum(dO*O), [B,H,N]
   float* part[kMaxP][3];   // fp32 partial dQ, dK, dV of pattern p, [B,H,N/r,D] sparse order
   void* dq;                // outputs, input dtype, strides sb/sn/sh
   void* dk;
@@ -160,7 +160,7 @@ struct BwdPrepArgs {
   const void* o;
   const void* dout;
   const float* lse;        // combined LSE [B,H,N]
-  float2* ld;              // out: (LSE * log2 e, D) [B,H,N]
+  float2* ld;              // out: (-LSE * log2 e, -D) [B,H,N]
   void* dq;
   void* dk;
   void* dv;

@@ -53,7 +53,7 @@ struct Plan {
   size_t part_o_off[kMaxP];
   size_t part_lse_off[kMaxP];
   size_t ws_fwd;
-  // backward workspace: (LSE * log2 e, D = rowsum(dO*O)) [B,H,N] float pairs;
+  // backward workspace: (-LSE * log2 e, -D), D = rowsum(dO*O), [B,H,N] float pairs;
   // with several patterns, per pattern the fp32 partial dQ, dK, dV [B,H,N/r,D]
   // in sparse order (only rows that another pattern also keeps are written)
   size_t ld_off;

@@ -38,7 +38,7 @@ hipError_t launch_shard_gather(const ShardGatherArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The (LSE * log2 e, D) pairs of the same rows: out[(b*H + h)*out_rows +
+// The (-LSE * log2 e, -D) pairs of the same rows: out[(b*H + h)*out_rows +
 // out_row0 + i] = ld[(b*H + h)*N + (h mod r) + i*r].
 __global__ __launch_bounds__(256) void shard_ld_kernel(const ShardLdArgs a) {
   const int64_t total = a.B * a.H * a.cr;
