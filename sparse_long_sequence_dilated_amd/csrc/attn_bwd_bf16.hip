@@ -116,6 +116,9 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     nl2_own = x.x;
     nd_own = x.y;
   }
+  f32x16 nd_tile;  // query units: -D of the lane's query in every element (dP's starting value)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) nd_tile[e] = nd_own;
 
   // Streamed range: tiles t = 0..nt-1 start at row 64*(t_first + t); half h
   // covers streamed rows s0(h) = 64*t_first + 32h .. +32.
@@ -199,14 +202,14 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
 
   // ---- pipeline stages ------------------------------------------------------
   // S and dP of half hh (blk = hh & 1 within its tile).
-  // Key units start the dP accumulator at -D of each element's query, so
-  // that dS = P (dP - D) is one multiply.  (Element e = 4g + i of a lane is
-  // streamed row 32 blk + 8g + 4 lg + i.)
+  // The dP accumulator starts at -D of each element's query (key units: from
+  // the tile's -D run; query units: the lane's own -D), so that
+  // dS = P (dP - D) is one multiply.  (In key units element e = 4g + i of a
+  // lane is streamed row 32 blk + 8g + 4 lg + i.)
   auto ld_offset = [&](int blk, int g) __attribute__((always_inline)) {
     return 4 * (32 * (2 * blk + (g >> 1)) + 8 * (g & 1) + 4 * lg);  // bytes; D 64 bytes later
   };
   auto stage_sd = [&](const BwdStage* __restrict__ st, int blk, f32x16& S, f32x16& P) __attribute__((always_inline)) {
-    S = f32x16{};
     if (kKV) {
       typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 #pragma unroll
@@ -215,15 +218,13 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
 #pragma unroll
         for (int i = 0; i < 4; ++i) P[4 * g + i] = nd[i];
       }
-    } else {
-      P = f32x16{};
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 xa = lds_read_b128((const lds_u4*)st->a, blk * 4096 + roff[ks]);
       const bf16x8 xb = lds_read_b128((const lds_u4*)st->b, blk * 4096 + roff[ks]);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, opa[ks], S, 0, 0, 0);
-      P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, opb[ks], P, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, opa[ks], ks ? S : f32x16{}, 0, 0, 0);
+      P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, opb[ks], ks || kKV ? P : nd_tile, 0, 0, 0);
     }
   };
   // P and dS of half hh from its S and dP, packed to bf16 operand words.
@@ -254,7 +255,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
           if (dead) p = 0.f;
         }
         pv[i] = p;
-        dv[i] = kKV ? p * P[e] : p * (P[e] + nd_own);
+        dv[i] = p * P[e];
       }
       if (kKV) {
         pw[2 * g] = pack_bf16(pv[0], pv[1]);
@@ -309,7 +310,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * g + i;
       pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], c, nl[i]));
-      dv[i] = kKV ? pv[i] * P[e] : pv[i] * (P[e] + nd_own);
+      dv[i] = pv[i] * P[e];
     }
     if (kKV) {
       pw[2 * g] = pack_bf16(pv[0], pv[1]);
@@ -337,7 +338,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
       valu_chunk(ss, blk_v, q, S, P, pw, sw);
       acc0[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, words_bf16(swp, half), acc0[db], 0, 0, 0);
       Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, opa[q], q ? Sn : f32x16{}, 0, 0, 0);
-      Pn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, opb[q], q ? Pn : f32x16{}, 0, 0, 0);
+      Pn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb, opb[q], q ? Pn : nd_tile, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
