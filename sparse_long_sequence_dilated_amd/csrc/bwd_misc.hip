@@ -135,9 +135,11 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdFinalizeArgs
 // (batch, head) are kept by one set of patterns, so a workgroup of 32 such
 // rows has a uniform kept set; classes kept by fewer than two patterns are
 // skipped by whole workgroups and each lane loads only the kept partials.
-// Grid: (row blocks, R, B*H).
+// A workgroup sums one of the three gradients; the patterns go in groups of
+// four whose loads issue before the group's adds (which keep descriptor
+// order).  Grid: (row blocks, R, 3*B*H).
 __global__ __launch_bounds__(256) void bwd_finalize_class_kernel(const BwdFinalizeArgs a) {
-  const uint32_t bhu = blockIdx.z;
+  const uint32_t g = blockIdx.z % 3u, bhu = blockIdx.z / 3u;
   const uint32_t h = bhu % (uint32_t)a.H, b = bhu / (uint32_t)a.H;
   const uint32_t rho = blockIdx.y;
   uint32_t kept = 0;
@@ -148,48 +150,49 @@ __global__ __launch_bounds__(256) void bwd_finalize_class_kernel(const BwdFinali
   }
   const bool span = (kept & a.span_mask) != 0;      // see bwd_finalize_kernel
   if (__builtin_popcount(kept) < 2 && !span) return;
+  if (span && g != 0) return;                        // dK, dV of such rows: the shard finish pass
   const uint32_t t = blockIdx.x * 32 + (threadIdx.x >> 3);
   if (t >= a.rows_per_class) return;
   const int c = threadIdx.x & 7;
   const uint32_t n = rho + a.R * t;
   if (n >= (uint32_t)batch_len(a.lengths, b, a.N)) return;  // padding rows were zeroed
   const int64_t bh = (int64_t)b * a.H + h;
-  const int64_t out_off = (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
-  float acc[3][8];
+  float acc[8];
 #pragma unroll
-  for (int g = 0; g < 3; ++g)
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int p0 = 0; p0 < a.P; p0 += 4) {
+    float4 x[4], y[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
-  for (int p = 0; p < a.P; ++p) {
-    if (!((kept >> p) & 1u)) continue;                 // uniform
-    const uint32_t rp = (uint32_t)a.r[p];
-    const int64_t row = bh * a.nsp[p] + rho / rp + (a.R / rp) * t;
-    float4 x[3], y[3];
-#pragma unroll
-    for (int g = 0; g < 3; ++g) {
-      const float* src = a.part[p][g] + row * kD + 8 * c;
-      x[g] = *(const float4*)src;
-      y[g] = *(const float4*)(src + 4);
+    for (int j = 0; j < 4; ++j) {
+      const int p = p0 + j;
+      if (p < a.P && ((kept >> p) & 1u)) {            // uniform
+        const uint32_t rp = (uint32_t)a.r[p];
+        const int64_t row = bh * a.nsp[p] + rho / rp + (a.R / rp) * t;
+        const float* src = a.part[p][g] + row * kD + 8 * c;
+        x[j] = *(const float4*)src;
+        y[j] = *(const float4*)(src + 4);
+      }
     }
 #pragma unroll
-    for (int g = 0; g < 3; ++g) {
-      acc[g][0] += x[g].x; acc[g][1] += x[g].y; acc[g][2] += x[g].z; acc[g][3] += x[g].w;
-      acc[g][4] += y[g].x; acc[g][5] += y[g].y; acc[g][6] += y[g].z; acc[g][7] += y[g].w;
+    for (int j = 0; j < 4; ++j) {
+      const int p = p0 + j;
+      if (p < a.P && ((kept >> p) & 1u)) {
+        acc[0] += x[j].x; acc[1] += x[j].y; acc[2] += x[j].z; acc[3] += x[j].w;
+        acc[4] += y[j].x; acc[5] += y[j].y; acc[6] += y[j].z; acc[7] += y[j].w;
+      }
     }
   }
-#pragma unroll
-  for (int g = 0; g < 3; ++g)
-    if (g == 0 || !span)
-      *(uint4*)((__bf16*)a.grad[g] + out_off) =
-          uint4{pack_bf16(acc[g][0], acc[g][1]), pack_bf16(acc[g][2], acc[g][3]),
-                pack_bf16(acc[g][4], acc[g][5]), pack_bf16(acc[g][6], acc[g][7])};
+  const int64_t out_off = (int64_t)b * a.sb + (int64_t)n * a.sn + (int64_t)h * a.sh + 8 * c;
+  *(uint4*)((__bf16*)a.grad[g] + out_off) =
+      uint4{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
+            pack_bf16(acc[6], acc[7])};
 }
 
 hipError_t launch_bwd_finalize(const BwdFinalizeArgs& a, hipStream_t stream) {
   if (a.B * a.N * a.H == 0) return hipSuccess;
   TimedLaunch tl("bwd_finalize", stream);
-  if (a.R) {
-    const dim3 g((a.rows_per_class + 31) / 32, a.R, (unsigned)(a.B * a.H));
+  if (a.R && 3 * a.B * a.H <= 65535) {
+    const dim3 g((a.rows_per_class + 31) / 32, a.R, (unsigned)(3 * a.B * a.H));
     hipLaunchKernelGGL(bwd_finalize_class_kernel, g, dim3(256), 0, stream, a);
   } else {
     const dim3 grid((unsigned)(a.B * a.nblk), (unsigned)a.H);
