@@ -1,7 +1,8 @@
 // Backward preprocessing: D = rowsum(dO * O) per (batch, head, row), stored
-// next to the combined LSE (pre-multiplied by log2 e) so that the attention
-// backward fetches both with one 8-byte load per row; and zero gradients for
-// rows that no pattern keeps (their output is the constant 0).
+// negated next to the negated combined LSE (pre-multiplied by log2 e) so
+// that the attention backward fetches both with one 8-byte load per row and
+// can start its dP accumulator at -D; and zero gradients for rows that no
+// pattern keeps (their output is the constant 0).
 // Eight lanes per (b, n, h) row, eight d values each; rows walked in
 // [B, N, H] order so that O and dO are read contiguously.  HBM bound.
 #include "dla_device.h"
