@@ -343,6 +343,28 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     }
   };
 
+  // Steady state of a key unit: gradient products of half hh-1 (dV and dK
+  // of one head-dim block and 16-query step per group) interleaved with the
+  // P/dS work of half hh, four groups separated by scheduling fences.  A
+  // group issues the LDS reads of its two transposed operands, then its
+  // four elements of VALU work (which cover the read latency), then its two
+  // MFMAs, which run while the next group's VALU issues.
+  auto fused_kv = [&](const BwdStage* __restrict__ sg, int blk_g, const uint32_t (&pwp)[8],
+                      const uint32_t (&swp)[8], const BwdStage* __restrict__ sv, int blk_v,
+                      const f32x16& S, const f32x16& P, uint32_t (&pw)[8], uint32_t (&sw)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int half = q >> 1, db = q & 1;
+      const int kko = (2 * blk_g + half) * 2048;
+      const bf16x8 dta = lds_read_tr8((const lds_u4*)sg->b, tlo[db] + kko, thi[db] + kko);
+      const bf16x8 qta = lds_read_tr8((const lds_u4*)sg->a, tlo[db] + kko, thi[db] + kko);
+      valu_chunk(sv, blk_v, q, S, P, pw, sw);
+      acc1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dta, words_bf16(pwp, half), acc1[db], 0, 0, 0);
+      acc0[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, words_bf16(swp, half), acc0[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   f32x16 sx, px, sy, py;                       // S, dP of the even (x) / odd (y) half in flight
   uint32_t pwx[8], swx[8], pwy[8], swy[8];     // packed P, dS of the even / odd half
 
@@ -365,7 +387,9 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
     if (!kKV && a_prev && a_cur && a_next && !msk) {                                             \
       fused_q(sg, 1 - (blk), sw_prv, ss, 1 - (blk), S_nxt, P_nxt, blk, S_cur, P_cur, pw_cur, sw_cur); \
     } else {                                                                                     \
-      if (kKV && a_prev && a_cur && !msk) {                                                      \
+      if (kKV && !kWin && a_prev && a_cur && !msk) {                                             \
+        fused_kv(sg, 1 - (blk), pw_prv, sw_prv, sv, blk, S_cur, P_cur, pw_cur, sw_cur);          \
+      } else if (kKV && a_prev && a_cur && !msk) {                                               \
         stage_grad(sg, 1 - (blk), pw_prv, sw_prv);                                               \
         stage_valu(hh, sv, blk, S_cur, P_cur, false, pw_cur, sw_cur);                            \
         DLA_INTERLEAVE(8, 10);                                                                   \
