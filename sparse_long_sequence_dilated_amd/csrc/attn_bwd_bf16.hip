@@ -523,8 +523,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_bf16_kernel(const AttnBwdArgs
   const bool kv = u < (uint32_t)a.sched_kv.total;
   int p, b, h, tile;
   int64_t seg;
-  decode_unit(kv ? a.sched_kv : a.sched_q, kv ? u : u - (uint32_t)a.sched_kv.total, (int)a.H, a.nseg,
-              p, b, h, seg, tile);
+  if (!decode_unit(kv ? a.sched_kv : a.sched_q, kv ? u : u - (uint32_t)a.sched_kv.total, (int)a.H, a.nseg,
+                   p, b, h, seg, tile))
+    return;
   if (kv) {
     if (a.causal) tile = (a.L[p] + kBwdRows - 1) / kBwdRows - 1 - tile;
     bwd_unit<true, kWin>(a, ring, p, b, h, seg, tile);

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
 
   int p, b, h, tile;
   int64_t seg;
-  decode_unit(a.sched, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile);
+  if (!decode_unit(a.sched, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile)) return;
   // L query rows (local), Lk key rows; local query row i is row qoff + i of
   // the segment (qoff = 0 and Lk = L except for a segment that spans
   // several sequence shards, whose keys come from the gathered buffers).

@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const AttnFwdArgs a) 
   const int tid = threadIdx.x;
   int p, b, h, tile;
   int64_t seg;
-  decode_unit(a.sched, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile);
+  if (!decode_unit(a.sched, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile)) return;
   const int w = a.w[p], r = a.r[p], L_full = a.L[p];
   // fewer in a cut-short last segment (of the sequence or of this batch's)
   const int L = seg_rows(batch_len(a.lengths, b, a.N), seg, w, r, h, L_full);

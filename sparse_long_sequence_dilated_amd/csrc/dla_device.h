@@ -42,12 +42,16 @@ __device__ __forceinline__ int seg_rows(int64_t N, int64_t seg, int w, int r, in
   return left > off ? (int)((left - 1 - off) / r) + 1 : 0;
 }
 
-// Longest-first unit decode (see Schedule in dla_plan.h).  All quantities fit
+// Longest-first unit decode (see Schedule in dla_plan.h); false for an empty
+// unit (a group past a pattern's last segment-head).  All quantities fit
 // in 32 bits (the planner bounds the unit count by the launch grid), so the
 // divisions are 32-bit.
-__device__ __forceinline__ void decode_unit(const Schedule& s, uint32_t u, int H,
+__device__ __forceinline__ bool decode_unit(const Schedule& s, uint32_t u, int H,
                                             const int64_t* nseg, int& p, int& b, int& h,
                                             int64_t& seg, int& tile) {
+  const uint32_t upg = (uint32_t)s.upg;
+  const uint32_t grp = u / upg;
+  u -= grp * upg;
   int j = 0;
   while (j + 1 < s.nband && u >= (uint32_t)s.band_start[j + 1]) ++j;
   const uint32_t rel = u - (uint32_t)s.band_start[j];
@@ -60,11 +64,15 @@ __device__ __forceinline__ void decode_unit(const Schedule& s, uint32_t u, int H
   p = s.order[i];
   rem -= (uint32_t)s.cum[i];
   const uint32_t ns = (uint32_t)nseg[p];
-  const uint32_t sg = rem % ns;
-  rem /= ns;
-  h = (int)(rem % (uint32_t)H);
-  b = (int)(rem / (uint32_t)H);
+  const int64_t gi = (int64_t)grp * s.chunk[p] + rem;  // segment-head index within the pattern
+  if (gi >= s.count[p]) return false;                   // past the pattern's last one
+  uint32_t g32 = (uint32_t)gi;
+  const uint32_t sg = g32 % ns;
+  g32 /= ns;
+  h = (int)(g32 % (uint32_t)H);
+  b = (int)(g32 / (uint32_t)H);
   seg = sg;
+  return true;
 }
 
 // Bit-cast helpers.

@@ -202,17 +202,34 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
   return DLA_OK;
 }
 
+// Streamed bytes per group of the schedule: the rows that the units of a
+// group re-stream (two tensors of L rows per segment-head) should stay in
+// the 256 MB last-level cache while the group runs.  At 1M tokens this took
+// the forward from 9.30 to 8.52 ms and at 2 x 32K tokens the backward from
+// 1.85 to 1.79 ms; 96 MB measured the same and 48 MB slower.
+constexpr double kGroupBytes = 192.0 * (1 << 20);
+
 void make_schedule(const Plan& p, int tile_rows, Schedule* s) {
   memset(s, 0, sizeof(*s));
+  const double budget = kGroupBytes;
+  double bytes = 0;
+  for (int i = 0; i < p.P; ++i) bytes += (double)p.B * p.H * p.nseg[i] * p.L[i] * kD * p.esize * 2;
+  int64_t groups = std::max<int64_t>(1, (int64_t)ceil(bytes / budget));
+  int64_t most = 0;
+  for (int i = 0; i < p.P; ++i) most = std::max<int64_t>(most, p.B * p.H * p.nseg[i]);
+  groups = std::max<int64_t>(1, std::min<int64_t>(groups, most));
+  s->groups = groups;
   int ntile[kMaxP];
   for (int i = 0; i < p.P; ++i) {
     ntile[i] = (p.L[i] + tile_rows - 1) / tile_rows;
     s->order[i] = i;
+    s->count[i] = p.B * p.H * p.nseg[i];
+    s->chunk[i] = (s->count[i] + groups - 1) / groups;
   }
   std::stable_sort(s->order, s->order + p.P,
                    [&](int a, int b) { return ntile[a] > ntile[b]; });
   s->cum[0] = 0;
-  for (int i = 0; i < p.P; ++i) s->cum[i + 1] = s->cum[i] + p.B * p.H * p.nseg[s->order[i]];
+  for (int i = 0; i < p.P; ++i) s->cum[i + 1] = s->cum[i] + s->chunk[s->order[i]];
   int64_t start = 0;
   int nb = 0;
   for (int i = 0; i < p.P; ++i) {
@@ -227,7 +244,8 @@ void make_schedule(const Plan& p, int tile_rows, Schedule* s) {
   }
   s->band_start[nb] = start;
   s->nband = nb;
-  s->total = start;
+  s->upg = start;
+  s->total = start * groups;
 }
 
 }  // namespace dla

@@ -26,6 +26,15 @@ struct Schedule {
   int band_npat[kMaxP];         // patterns active in the band (a prefix of `order`)
   int64_t band_start[kMaxP + 1];
   int64_t total;                // number of units
+  // The (batch, head, segment) units of every pattern are split into
+  // `groups` equal runs, scheduled one after another (each longest first):
+  // group j holds segment-heads j*chunk[p] .. (j+1)*chunk[p]-1 of pattern p,
+  // so that a group's keys and values stay cache-resident while its units
+  // re-stream them.  Units past a pattern's last segment-head are empty.
+  int64_t groups;
+  int64_t upg;                  // units per group
+  int64_t chunk[kMaxP];         // segment-heads of each pattern per group
+  int64_t count[kMaxP];         // segment-heads of each pattern: B * H * nseg
 };
 
 struct Plan {
