@@ -147,3 +147,28 @@ def test_forward_c4_sampled_rows():
         eo, el = normwise(o_got, o_ref), normwise(l_got, l_ref)
         print(f"C4 head {h}: O {eo:.3e} LSE {el:.3e}", flush=True)
         assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+def test_forward_grouped_schedule_cut_short_sampled_rows():
+    """A problem large enough for several cache-sized schedule groups (each
+    pattern's segment-heads split into runs, some units of the last run
+    empty), with a cut-short last segment; sampled rows of both batches."""
+    import torch
+    B, N, H = 2, 65000, 12
+    pats = ((2048, 1), (4096, 2), (16384, 8))
+    q, k, v = inputs.random_case(6500, B, N, H, "bf16")
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    o, lse = dla.forward(tq, tk, tv, pats, True, 0.125)
+    torch.cuda.synchronize()
+    del tq, tk, tv
+    g = np.random.default_rng(7)
+    special = [0, 2047, 2048, 16383, 16384, 49152, 63487, 63488, 64511, 64512, N - 2, N - 1]
+    for b in (0, 1):
+        for h in (0, 7, 11):
+            rows = np.unique(np.concatenate([special, g.integers(0, N, 24)]))
+            o_ref, l_ref = oracle.forward_rows(q, k, v, pats, True, 0.125, b, h, rows)
+            idx = torch.from_numpy(rows).cuda()
+            eo = normwise(o[b, :, h][idx].float().cpu().numpy(), o_ref)
+            el = normwise(lse[b, h][idx].cpu().numpy(), l_ref)
+            print(f"grouped N={N} b={b} h={h}: O {eo:.3e} LSE {el:.3e}", flush=True)
+            assert eo <= TOL["bf16"] and el <= TOL["bf16"]
