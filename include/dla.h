@@ -29,14 +29,18 @@
  *     is shape->dtype (fp32 or bf16; bf16 paths compute in bf16 with fp32
  *     accumulation).  lse is a device pointer to a contiguous fp32 [B, H, N]
  *     tensor holding natural-log log-sum-exp values.
- *   - All device pointers and strides*element size must be 16-byte aligned.
- *     An empty problem (B == 0 or H == 0) reads and writes nothing, so its
- *     pointers are not checked and may be null.
+ *   - All device pointers and strides*element size must be 16-byte aligned,
+ *     unless an entry point states otherwise (the FP8 codes and scales, the
+ *     lengths array).  An empty problem (B == 0 or H == 0) reads and writes
+ *     nothing, so its pointers are not checked and may be null.
  *   - The caller owns every buffer, including the workspace; the library
- *     allocates and frees nothing, keeps no device state and never
+ *     allocates and frees no device memory, keeps no device state and never
  *     synchronises (apart from dla_timing_collect, which waits for its
- *     events).  Work is enqueued on `stream` (a hipStream_t; NULL is the
- *     null stream) and returns before it runs.
+ *     events).  The exceptions are the attention layer's calls:
+ *     dla_blas_create makes a hipBLASLt handle (its own host and device
+ *     state), and each layer call creates and destroys hipBLASLt's small
+ *     host-side descriptors.  Work is enqueued on `stream` (a hipStream_t;
+ *     NULL is the null stream) and returns before it runs.
  *   - Descriptors are caller-owned host memory read only during the call.
  *   - Return value: DLA_OK or a negative DLA_E_* code.  All validation runs on
  *     the host before anything is enqueued; a failed call enqueues nothing.
