@@ -18,6 +18,9 @@ Also reported, as extra fields of the same line:
   * `layer`: the attention layer around the operator (hipBLASLt projections,
     768 dimensions, 12 heads, random weights) at 16 x 2K and 1 x 32K tokens,
     forward and forward plus backward;
+  * `cold_cache` (the step, and each forward line): kernel time per step when
+    512 MB are written between steps, so no input stays in the 256 MB
+    last-level cache (`value` is the warm, back-to-back step);
   * `roofline` of the kernel family that takes most of the timed region,
     timed live with HIP events around its launches on the launch stream;
   * `cpu_baseline`: the CPU oracle (float32, thread pool) on a bounded
@@ -138,6 +141,30 @@ def time_steps(step, steps, warmup):
     return (t1 - t0) * 1e3 / steps, fams
 
 
+def cold_kernel_ms(step, steps, flush_bytes=512 << 20):
+    """Kernel time per step (the library's HIP-event-timed launches) when a
+    write of `flush_bytes` between steps evicts the 256 MB last-level cache,
+    so that every step starts with its inputs in HBM only."""
+    import torch
+    from sparse_long_sequence_dilated_amd import dla
+    buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    step()
+    torch.cuda.synchronize()
+    total = 0.0
+    for i in range(steps):
+        buf.fill_(i & 0xFF)
+        torch.cuda.synchronize()
+        dla.timing_enable(True)
+        step()
+        torch.cuda.synchronize()
+        dla.timing_enable(False)
+        for fam in ("attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "combine", "bwd_prep", "attn_bwd",
+                    "bwd_finalize", "shard_gather", "shard_finish", "quantize_fp8"):
+            total += dla.timing_collect(fam)[1]
+    del buf
+    return total / steps
+
+
 def forward_only(name, steps, warmup):
     import torch
     from sparse_long_sequence_dilated_amd import dla, inputs
@@ -158,6 +185,9 @@ def forward_only(name, steps, warmup):
            "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS}
     for fam, (n, fms) in fams.items():
         out[f"{fam}_us_per_launch"] = 1e3 * fms / n
+    cold = cold_kernel_ms(step, min(steps, 10))
+    out["cold_cache"] = {"kernel_ms": cold, "tokens_per_s": wl.B * wl.N / (cold * 1e-3),
+                         "pct_bf16_peak": 100.0 * 4 * wl.D * pairs / (cold * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return out
@@ -414,6 +444,7 @@ def main():
                 "work_per_step": work, "work_unit": unit}
     kernels = {f: {"launches_per_step": n / args.steps, "us_per_step": 1e3 * t / args.steps}
                for f, (n, t) in fams.items()}
+    cold = cold_kernel_ms(step, min(args.steps, 10))
     del tensors, q, k, v, do, ws_fwd, ws_bwd, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
 
@@ -436,6 +467,8 @@ def main():
                    "step": "dla_forward + dla_backward" if wl.backward else "dla_forward"},
         "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
         "roofline": roofline, "kernels": kernels, "forward_only": extra, "cpu_baseline": cpu,
+        "cold_cache": {"kernel_ms_per_step": cold, "tokens_per_s": wl.B * wl.N / (cold * 1e-3),
+                       "note": "512 MB written between steps; kernel time only"},
     }
     if not args.no_forward_lines:
         line["shard_forward"] = shard
