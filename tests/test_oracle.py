@@ -449,3 +449,38 @@ def test_varlen_pair_count_matches_brute_force(causal):
     want = sum(oracle.multiplicity(n_b, pats, causal, h).sum() for n_b in lens if n_b
                for h in range(5))
     assert oracle.pair_count(len(lens), 40, 5, pats, causal, lengths=lens) == want
+
+
+def _hops_to_connect(N, pats, heads, causal):
+    """Fewest attention hops after which every row reaches every (earlier) row,
+    a hop going from a query to a key that some head and pattern let it see
+    (the heads are mixed between layers); None if some pair never connects."""
+    A = np.zeros((N, N), dtype=bool)
+    for h in range(heads):
+        A |= oracle.multiplicity(N, pats, causal, h) > 0
+    target = np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
+    R, hops = A.copy(), 1
+    while not R[target].all():
+        grown = ((R.astype(np.int64) @ A.astype(np.int64)) > 0) | R
+        if np.array_equal(grown, R):
+            return None
+        R, hops = grown, hops + 1
+    return hops
+
+
+@pytest.mark.parametrize("w0,levels", [(2, 5), (4, 6), (8, 6)])
+def test_geometric_patterns_connect_rows_in_logarithmic_hops(w0, levels):
+    """gptget.net page, 方法详解 (sixth item) and the darcstar.tech commentary:
+    local attention plus dilated global sampling keeps the path between any
+    two tokens logarithmic.  With the geometric schedule (w0 2^i, 2^i) over
+    N = w0 2^(levels-1) and every head offset present, every row reaches
+    every other row within log2(N / w0) + 1 hops, while the local pattern
+    alone never leaves its segment."""
+    N = w0 * 2 ** (levels - 1)
+    pats = inputs.geometric_patterns(w0, 2, levels)
+    hops = _hops_to_connect(N, pats, 2 ** (levels - 1), causal=False)
+    assert hops is not None and hops <= levels
+    assert _hops_to_connect(N, [(w0, 1)], 1, causal=False) is None
+    # under the causal mask a row cannot reach an earlier row that a later
+    # key between them never sees: e.g. row w0 (first of its block) and row w0-1
+    assert _hops_to_connect(N, pats, 2 ** (levels - 1), causal=True) is None
