@@ -128,11 +128,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const float lse = mx + logf(tot);
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const float wt = (kept >> p) & 1u ? expf(lv[p] - lse) : 0.f;
+    // A pattern that does not keep the row is discarded by selection, not by
+    // a zero weight: its load read o itself (the primary pattern's slot,
+    // which the primary never wrote for this row) or entry 0 of a partial
+    // buffer, and 0 * (NaN or inf) would poison the sum.
+    const bool k = (kept >> p) & 1u;
+    const float wt = k ? expf(lv[p] - lse) : 0.f;
     float v[8];
     Vec8<T>::unpack(raw[p], v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wt, v[i], acc[i]);
+    for (int i = 0; i < 8; ++i) acc[i] = k ? __builtin_fmaf(wt, v[i], acc[i]) : acc[i];
   }
   Vec8<T>::store(orow, acc);
   if (c == 0) *lse_dst = lse;

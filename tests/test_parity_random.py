@@ -1,0 +1,64 @@
+"""Randomized GPU property tests (needs an MI355X).
+
+Seeded random shapes and pattern sets, small enough for the brute-force
+form: N in 1..300 (ragged, cut-short segments, w > N), 1..6 heads, 1..4
+patterns with rates 1..8 (so r > H and uncovered rows occur), causal or not,
+bf16 or fp32.  The forward is compared with the union-softmax brute force
+(an independent formulation of the operator), and the bf16 backward with the
+oracle's analytic gradients.  Outputs start filled with NaN, so an entry
+the library fails to write is caught whatever memory held before.  Every
+call goes through the C ABI.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_long_sequence_dilated_amd import dla, inputs
+from tests.gpu_util import TOL, normwise, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed):
+    g = np.random.default_rng(seed)
+    B = int(g.integers(1, 3))
+    N = int(g.integers(1, 301))
+    H = int(g.integers(1, 7))
+    pats = []
+    for _ in range(int(g.integers(1, 5))):
+        r = int(g.choice([1, 2, 3, 4, 8]))
+        L = int(g.integers(1, 80))
+        pats.append((r * L, r))
+    causal = bool(g.integers(0, 2))
+    dtype = "f32" if seed % 4 == 3 else "bf16"
+    return B, N, H, tuple(pats), causal, dtype
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_case_against_brute_force(seed):
+    import torch
+    B, N, H, pats, causal, dtype = _case(seed)
+    print(f"seed {seed}: B={B} N={N} H={H} patterns={pats} causal={causal} {dtype}", flush=True)
+    q, k, v, dout = inputs.random_case(9000 + seed, B, N, H, dtype, count=4)
+    scale = 0.125
+    tq, tk, tv, tdo = (to_device(x, dtype) for x in (q, k, v, dout))
+    # outputs start as NaN, so an entry the library never writes cannot pass
+    o = torch.full_like(tq, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    dla.forward(tq, tk, tv, pats, causal, scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_bf, lse_bf = oracle.brute_force_forward(q, k, v, pats, causal, scale)
+    eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
+    print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
+    assert eo <= TOL[dtype] and el <= TOL[dtype]
+    if dtype != "bf16":
+        return
+    dq, dk, dv = (torch.full_like(tq, float("nan")) for _ in range(3))
+    dla.backward(tq, tk, tv, o, lse, tdo, pats, causal, scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, scale)
+    refs = oracle.backward(q, k, v, o_ref, lse_ref, dout, pats, causal, scale)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        e = normwise(to_host(got), ref)
+        print(f"  {name} {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], (name, e)
