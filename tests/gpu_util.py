@@ -42,3 +42,17 @@ def normwise(x, ref):
         return 0.0
     den = np.abs(ref[fin]).max()
     return float(np.abs(x[fin] - ref[fin]).max() / (den if den > 0 else 1.0))
+
+
+def nan_like(t):
+    """A NaN-filled tensor with t's shape, strides and dtype: passed as an output
+    buffer, any entry the library fails to write stays NaN and fails the check."""
+    import torch
+    return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device).fill_(float("nan"))
+
+
+def nan_lse(q):
+    """A NaN-filled [B, H, N] float32 log-sum-exp buffer for q of shape [B, N, H, D]."""
+    import torch
+    B, N, H, _ = q.shape
+    return torch.full((B, H, N), float("nan"), dtype=torch.float32, device=q.device)

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from sparse_long_sequence_dilated_amd import dla, inputs
-from tests.gpu_util import ORACLE_WORKERS, TOL, normwise, to_device, to_host
+from tests.gpu_util import ORACLE_WORKERS, TOL, nan_like, nan_lse, normwise, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,8 @@ SMALL = [
 def _check_forward(q, k, v, pats, causal, scale, dtype, layout="bnhd", workers=1,
                    ref_dtype=np.float64):
     tq, tk, tv = (to_device(x, dtype, layout) for x in (q, k, v))
-    o, lse = dla.forward(tq, tk, tv, pats, causal, scale)
+    o, lse = nan_like(tq), nan_lse(tq)
+    dla.forward(tq, tk, tv, pats, causal, scale, out=o, lse=lse)
     import torch
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, scale, dtype=ref_dtype, workers=workers)

@@ -41,12 +41,21 @@ def _run_shards(tq, tk, tv, pats, causal, scale, N, total):
                 ext_k[p] = _gathered(tk, pats, p, N, total, g)
                 ext_v[p] = _gathered(tv, pats, p, N, total, g)
         sl = slice(g * N, (g + 1) * N)
-        o, lse = dla.forward_shard(tq[:, sl], tk[:, sl], tv[:, sl], pats, total, g * N, ext_k, ext_v,
-                                   causal, scale)
+        # outputs start as NaN, so an entry the library never writes cannot pass
+        o = _nan_like(tq[:, sl])
+        lse = torch.full((tq.shape[0], tq.shape[2], N), float("nan"), device="cuda")
+        dla.forward_shard(tq[:, sl], tk[:, sl], tv[:, sl], pats, total, g * N, ext_k, ext_v,
+                          causal, scale, out=o, lse=lse)
         outs.append(o)
         lses.append(lse)
     torch.cuda.synchronize()
     return torch.cat(outs, dim=1), torch.cat(lses, dim=2)
+
+
+def _nan_like(t):
+    """A NaN-filled tensor with t's shape and strides (the library's outputs share q's layout)."""
+    import torch
+    return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device).fill_(float("nan"))
 
 
 def test_shard_gather_is_exact():
@@ -151,8 +160,10 @@ def test_backward_shards_match_whole_sequence_oracle(case):
         ext_v = {p: _gathered(tv, pats, p, N, total, g) for p in span}
         o, lse = dla.forward_shard(tq[:, sl], tk[:, sl], tv[:, sl], pats, total, g * N, ext_k, ext_v,
                                    causal, 0.125)
+        nan = [_nan_like(tq[:, sl]) for _ in range(3)]
         first.append(dla.backward_shard(tq[:, sl], tk[:, sl], tv[:, sl], o, lse, tdo[:, sl], pats,
-                                        total, g * N, ext_k, ext_v, causal, 0.125))
+                                        total, g * N, ext_k, ext_v, causal, 0.125,
+                                        dq=nan[0], dk=nan[1], dv=nan[2]))
     # the exchange: device g of a segment gets the sum over the segment's devices of their parts
     dqs, dks, dvs = [], [], []
     for g in range(G):

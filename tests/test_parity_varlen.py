@@ -38,7 +38,10 @@ def test_varlen_forward_and_backward(case):
     B = len(lens)
     q, k, v, dout = inputs.random_case(zlib.crc32(repr(case).encode()) & 0xFFFF, B, N, H, dtype, count=4)
     tq, tk, tv, tdo = (to_device(x, dtype) for x in (q, k, v, dout))
-    o, lse = dla.forward_varlen(tq, tk, tv, lens, pats, causal, 0.125)
+    # outputs start as NaN, so an entry the library never writes cannot pass
+    o = torch.full_like(tq, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    dla.forward_varlen(tq, tk, tv, lens, pats, causal, 0.125, out=o, lse=lse)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, 0.125, lengths=lens)
     eo, el = normwise(to_host(o), o_ref), normwise(to_host(lse), lse_ref)
@@ -48,7 +51,8 @@ def test_varlen_forward_and_backward(case):
         assert torch.all(o[b, n_b:] == 0) and torch.all(lse[b, :, n_b:] == float("-inf"))
     if dtype != "bf16":
         return
-    dq, dk, dv = dla.backward_varlen(tq, tk, tv, o, lse, tdo, lens, pats, causal, 0.125)
+    dq, dk, dv = (torch.full_like(tq, float("nan")) for _ in range(3))
+    dla.backward_varlen(tq, tk, tv, o, lse, tdo, lens, pats, causal, 0.125, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     refs = oracle.backward(q, k, v, o_ref, lse_ref, dout, pats, causal, 0.125, lengths=lens)
     for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
