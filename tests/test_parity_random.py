@@ -62,3 +62,30 @@ def test_random_case_against_brute_force(seed):
         e = normwise(to_host(got), ref)
         print(f"  {name} {e:.3e}", flush=True)
         assert e <= TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_varlen_case(seed):
+    """The same random cases (bf16) as batches of random lengths in 0..N."""
+    import torch
+    B, N, H, pats, causal, _ = _case(100 + seed)
+    lens = [int(x) for x in np.random.default_rng(200 + seed).integers(0, N + 1, B)]
+    print(f"seed {seed}: B={B} N={N} H={H} patterns={pats} causal={causal} lengths={lens}", flush=True)
+    q, k, v, dout = inputs.random_case(9500 + seed, B, N, H, "bf16", count=4)
+    tq, tk, tv, tdo = (to_device(x, "bf16") for x in (q, k, v, dout))
+    o = torch.full_like(tq, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    dla.forward_varlen(tq, tk, tv, lens, pats, causal, 0.125, out=o, lse=lse)
+    dq, dk, dv = (torch.full_like(tq, float("nan")) for _ in range(3))
+    dla.backward_varlen(tq, tk, tv, o, lse, tdo, lens, pats, causal, 0.125, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    o_bf, lse_bf = oracle.brute_force_forward(q, k, v, pats, causal, 0.125, lengths=lens)
+    eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
+    print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, 0.125, lengths=lens)
+    refs = oracle.backward(q, k, v, o_ref, lse_ref, dout, pats, causal, 0.125, lengths=lens)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        e = normwise(to_host(got), ref)
+        print(f"  {name} {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], (name, e)
