@@ -89,3 +89,30 @@ def test_random_varlen_case(seed):
         e = normwise(to_host(got), ref)
         print(f"  {name} {e:.3e}", flush=True)
         assert e <= TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_fp8kv_case(seed):
+    """Random cases with FP8 E4M3 keys and values: quantization bit-exact
+    against the oracle, the forward against the brute force on the decoded
+    keys and values."""
+    import torch
+    B, N, H, pats, causal, _ = _case(300 + seed)
+    print(f"seed {seed}: B={B} N={N} H={H} patterns={pats} causal={causal}", flush=True)
+    q, k, v = inputs.random_case(9700 + seed, B, N, H, "bf16")
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    k8, ks = dla.quantize_fp8(tk)
+    v8, vs = dla.quantize_fp8(tv)
+    o = torch.full_like(tq, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    dla.forward_fp8kv(tq, k8, v8, ks, vs, pats, causal, 0.125, out=o, lse=lse)
+    torch.cuda.synchronize()
+    kc, ksc = oracle.quantize_per_head(k)
+    vc, vsc = oracle.quantize_per_head(v)
+    assert np.array_equal(k8.cpu().numpy(), kc) and np.array_equal(ks.cpu().numpy(), ksc)
+    assert np.array_equal(v8.cpu().numpy(), vc) and np.array_equal(vs.cpu().numpy(), vsc)
+    kd, vd = oracle.dequantize_per_head(kc, ksc), oracle.dequantize_per_head(vc, vsc)
+    o_bf, lse_bf = oracle.brute_force_forward(q, kd, vd, pats, causal, 0.125)
+    eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
+    print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
