@@ -82,6 +82,14 @@ CASES = [
     (1, 4096, 3, ((512, 1), (4096, 2)), True, 2),                 # r = 1 local, two-device segment
     (1, 2048, 2, ((2048, 1),), True, 4),                          # one spanning pattern, r = 1
     (1, 2048, 13, ((2048, 4), (1024, 2)), True, 4),               # every pattern spans; uncovered rows
+    # drawn at random (local patterns with w | N, spanning ones with w = N 2^k, r | N and
+    # N / r a multiple of 128), kept when the planner accepts every shard
+    (2, 2048, 3, ((128, 1), (1024, 2)), True, 4),
+    (1, 2048, 3, ((1024, 4), (1024, 4), (2048, 2)), True, 2),     # duplicate local pattern
+    (1, 1024, 2, ((512, 1),), True, 4),
+    (2, 1024, 1, ((512, 2),), False, 4),
+    (1, 4096, 4, ((4096, 4), (2048, 1), (2048, 2)), True, 4),
+    (1, 4096, 5, ((4096, 2),), False, 4),
 ]
 
 
@@ -138,6 +146,10 @@ BWD_CASES = [
     (1, 4096, 3, ((512, 1), (4096, 2)), True, 2),
     (1, 2048, 2, ((2048, 1),), True, 4),
     (1, 2048, 13, ((2048, 4), (1024, 2)), True, 4),               # every pattern spans
+    (2, 2048, 3, ((128, 1), (1024, 2)), True, 4),                 # drawn at random (as above)
+    (1, 2048, 3, ((1024, 4), (1024, 4), (2048, 2)), True, 2),
+    (2, 1024, 1, ((512, 2),), False, 4),
+    (1, 4096, 4, ((4096, 4), (2048, 1), (2048, 2)), True, 4),
 ]
 
 
