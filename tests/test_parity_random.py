@@ -116,3 +116,44 @@ def test_random_fp8kv_case(seed):
     eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
     print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
     assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+def _large_case(seed):
+    g = np.random.default_rng(seed)
+    B = int(g.integers(1, 3))
+    N = int(g.integers(300, 3001))
+    H = int(g.integers(1, 5))
+    pats = []
+    for _ in range(int(g.integers(1, 4))):
+        r = int(g.choice([1, 2, 4, 3]))
+        L = int(g.integers(40, 700))
+        pats.append((r * L, r))
+    return B, N, H, tuple(pats), bool(g.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_larger_case(seed):
+    """Random cases of several 256-row query tiles and 64-row key tiles with
+    ragged tails (N up to 3000, L up to 700), bf16 forward against the brute
+    force and backward against the oracle."""
+    import torch
+    B, N, H, pats, causal = _large_case(400 + seed)
+    print(f"seed {seed}: B={B} N={N} H={H} patterns={pats} causal={causal}", flush=True)
+    q, k, v, dout = inputs.random_case(9900 + seed, B, N, H, "bf16", count=4)
+    tq, tk, tv, tdo = (to_device(x, "bf16") for x in (q, k, v, dout))
+    o = torch.full_like(tq, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    dla.forward(tq, tk, tv, pats, causal, 0.125, out=o, lse=lse)
+    dq, dk, dv = (torch.full_like(tq, float("nan")) for _ in range(3))
+    dla.backward(tq, tk, tv, o, lse, tdo, pats, causal, 0.125, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    o_bf, lse_bf = oracle.brute_force_forward(q, k, v, pats, causal, 0.125)
+    eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
+    print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, 0.125)
+    refs = oracle.backward(q, k, v, o_ref, lse_ref, dout, pats, causal, 0.125)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        e = normwise(to_host(got), ref)
+        print(f"  {name} {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], (name, e)
