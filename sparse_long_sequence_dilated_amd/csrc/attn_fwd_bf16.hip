@@ -96,10 +96,13 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   const int64_t rstride = (int64_t)r * a.sn;  // elements between consecutive sparse rows
   const __bf16* Qh = (const __bf16*)a.q + head_off + base_row * a.sn;
   const int64_t cr = a.nsp[p];                 // rows per gathered chunk
-  const __bf16* Kh = ext ? (const __bf16*)a.ext_k[p] + ((int64_t)b * a.H + h) * cr * kD
-                         : (const __bf16*)a.k + head_off + base_row * a.sn;
-  const __bf16* Vh = ext ? (const __bf16*)a.ext_v[p] + ((int64_t)b * a.H + h) * cr * kD
-                         : (const __bf16*)a.v + head_off + base_row * a.sn;
+  // bf16 keys and values (8-bit ones are addressed in bytes below)
+  const __bf16* Kh = kFp8 ? nullptr
+                   : ext  ? (const __bf16*)a.ext_k[p] + ((int64_t)b * a.H + h) * cr * kD
+                          : (const __bf16*)a.k + head_off + base_row * a.sn;
+  const __bf16* Vh = kFp8 ? nullptr
+                   : ext  ? (const __bf16*)a.ext_v[p] + ((int64_t)b * a.H + h) * cr * kD
+                          : (const __bf16*)a.v + head_off + base_row * a.sn;
   const int64_t kstride = ext ? (int64_t)kD : rstride;   // elements between key rows
 
   const int q0 = tile * kFwdBM;
@@ -142,7 +145,6 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   const int tiles_per_chunk = ext ? (int)(cr / kFwdBN) : 0x7FFFFFFF;
   const int64_t chunk_jump = ext ? ((int64_t)a.B * a.H - 1) * cr * kD * 2 : 0;
   int tc = 0;
-  // (With kFp8, Kh and Vh are byte pointers in the same element units.)
   const char* kcur = kFp8 ? (const char*)a.k + head_off + base_row * a.sn : (const char*)Kh;
   const char* vcur = kFp8 ? (const char*)a.v + head_off + base_row * a.sn : (const char*)Vh;
   auto issue_tile = [&](int kt, FwdStage* __restrict__ dst) __attribute__((always_inline)) {
