@@ -202,6 +202,47 @@ def forward_rows(q, k, v, patterns, causal, scale, b, h, rows, dtype=np.float64)
     return np.array(out_o, dtype), np.array(out_lse, dtype)
 
 
+def backward_dq_rows(q, k, v, dout, patterns, causal, scale, b, h, rows, dtype=np.float64):
+    """dQ of selected rows only ([len(rows), D]), for spot checks at sizes where
+    the full backward is too slow.
+
+    Row n's gradient needs only its own keys: for every pattern that keeps n
+    (head h), the rows of its dilated segment (at or before n if causal).
+    With the combined LSE and O of the row (as in `forward_rows`) and
+    D = dO_n . O_n, dQ_n = scale * sum over those (pattern, key) pairs of
+    P (dP - D) K_key, where P = exp(S - LSE) and dP = dO_n . V_key.
+    """
+    out = []
+    for n in rows:
+        n = int(n)
+        parts = []
+        for w, r in patterns:
+            if n % r != h % r:
+                continue
+            idx = segment_rows(q.shape[1], w, r, h, n // w)
+            if causal:
+                idx = idx[idx <= n]
+            parts.append(idx)
+        if not parts:
+            out.append(np.zeros(q.shape[-1], dtype))
+            continue
+        qn = np.asarray(q[b, n, h], dtype)
+        don = np.asarray(dout[b, n, h], dtype)
+        S = [scale * (np.asarray(k[b, idx, h], dtype) @ qn) for idx in parts]
+        m = max(s.max() for s in S)
+        den = sum(np.exp(s - m).sum() for s in S)
+        lse = m + np.log(den)
+        o = sum(np.exp(s - lse) @ np.asarray(v[b, idx, h], dtype) for s, idx in zip(S, parts))
+        d = don @ o
+        dq = np.zeros(q.shape[-1], dtype)
+        for s, idx in zip(S, parts):
+            P = np.exp(s - lse)
+            dP = np.asarray(v[b, idx, h], dtype) @ don
+            dq += scale * ((P * (dP - d)) @ np.asarray(k[b, idx, h], dtype))
+        out.append(dq)
+    return np.array(out, dtype)
+
+
 def backward(q, k, v, o, lse, dout, patterns, causal, scale, dtype=np.float64, workers=1,
              lengths=None):
     """Analytic gradients (dQ, dK, dV) of the combined forward w.r.t. q, k, v.

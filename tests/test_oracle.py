@@ -484,3 +484,18 @@ def test_geometric_patterns_connect_rows_in_logarithmic_hops(w0, levels):
     # under the causal mask a row cannot reach an earlier row that a later
     # key between them never sees: e.g. row w0 (first of its block) and row w0-1
     assert _hops_to_connect(N, pats, 2 ** (levels - 1), causal=True) is None
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_dq_rows_match_full_backward(causal):
+    """The row-at-a-time dQ equals the full backward's dQ rows (including
+    uncovered rows, cut-short segments and duplicate patterns)."""
+    pats = [(8, 1), (16, 2), (24, 4), (8, 1), (20, 5)]
+    q, k, v, dout = _rand(61, 2, 45, 3, 8, count=4)
+    o, lse = oracle.forward(q, k, v, pats, causal, 0.35)
+    dq, _, _ = oracle.backward(q, k, v, o, lse, dout, pats, causal, 0.35)
+    rows = np.arange(45)
+    for b in range(2):
+        for h in range(3):
+            got = oracle.backward_dq_rows(q, k, v, dout, pats, causal, 0.35, b, h, rows)
+            np.testing.assert_allclose(got, dq[b, :, h], rtol=1e-11, atol=1e-12)
