@@ -173,3 +173,26 @@ def test_forward_grouped_schedule_cut_short_sampled_rows():
             el = normwise(lse[b, h][idx].cpu().numpy(), l_ref)
             print(f"grouped N={N} b={b} h={h}: O {eo:.3e} LSE {el:.3e}", flush=True)
             assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+def test_forward_long_segment_sampled_rows():
+    """One segment of 65536 sparse rows (full causal attention over 64K rows:
+    256 query units and 1024 key tiles per segment-head), plus a dilated
+    pattern; sampled rows against the oracle one row at a time."""
+    import torch
+    B, N, H = 1, 65536, 2
+    pats = ((65536, 1), (65536, 4))
+    q, k, v = inputs.random_case(65536, B, N, H, "bf16")
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    o, lse = nan_like(tq), nan_lse(tq)
+    dla.forward(tq, tk, tv, pats, True, 0.125, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    rows = np.array([0, 1, 63, 64, 255, 256, 4097, 32767, 32768, 65279, 65280, 65535])
+    for h in (0, 1):
+        o_ref, l_ref = oracle.forward_rows(q, k, v, pats, True, 0.125, 0, h, rows)
+        idx = torch.from_numpy(rows).cuda()
+        eo = normwise(o[0, :, h][idx].float().cpu().numpy(), o_ref)
+        el = normwise(lse[0, h][idx].cpu().numpy(), l_ref)
+        print(f"long segment h={h}: O {eo:.3e} LSE {el:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and el <= TOL["bf16"]
