@@ -80,7 +80,8 @@ def family_work(family, wl, pairs):
         return 4 * D * pairs, "flop", "mfma"
     rows = wl.B * wl.N * wl.H
     if family == "bwd_prep":
-        return rows * (2 * D * 2 + 4), "byte", "hbm"    # read O, dO (bf16), write D (fp32)
+        # read O, dO (bf16) and LSE, write the (-LSE log2 e, -D) pair
+        return rows * (2 * D * 2 + 4 + 8), "byte", "hbm"
     if family == "bwd_finalize":
         # rows kept by k >= 2 patterns: read k fp32 partial rows of dQ, dK, dV,
         # write the three bf16 gradient rows

@@ -30,12 +30,12 @@
 // layout.  Half tile h runs as one phase:
 //   O^T += V_{h-1}^T P_{h-1} (4 MFMAs)  ||  P_h = exp2(S_h c - m)  (VALU)
 //   then S_{h+1} = K_{h+1} Q^T (4 MFMAs) into the registers S_h leaves free.
-// Softmax in the exp2 domain with a lazily updated offset: P is computed with
-// the current running maximum and accepted unless a lane's partial row sum
-// exceeds 2^16 (always the case on the first tile, where the offset is -inf);
-// then the true row maximum is taken, P recomputed, and the rescale of O and
-// l is applied before O's next update.  Row sums add the bf16-rounded P that
-// feeds the MFMA (v_dot2c_f32_bf16).
+// Softmax in the exp2 domain with a lazily updated offset: a wave's first
+// half tile sets it to the exact row maximum; later ones compute P with the
+// current offset and accept it unless a lane's partial row sum exceeds 2^16,
+// in which case the true row maximum is taken, P recomputed, and the rescale
+// of O and l is applied before O's next update.  Row sums add the
+// bf16-rounded P that feeds the MFMA (v_dot2c_f32_bf16).
 //
 // 8-bit keys and values (the quantization the gptget.net page, section
 // 方法详解, pairs with the method): K and V arrive as FP8 E4M3 codes with one
@@ -203,6 +203,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   float m_run = -INFINITY;                // running offset (log2 domain) of this lane's query
   float l_run = 0.f;                      // this lane's half of the row sum
   float pend = 1.f;                       // O rescale factor owed before O's next update
+  bool owed = false;                      // (wave-uniform) some lane's pend may differ from 1
 
   // ---- building blocks --------------------------------------------------------
   // K operand of step ks of S_h = K_h Q^T (half tile h in block blk of its stage).
@@ -227,8 +228,16 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
     const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 3], c, -m));
     pw[2 * g] = pack_bf16(x0, x1);
     pw[2 * g + 1] = pack_bf16(x2, x3);
-    r0 = dot2_bf16_ones(pw[2 * g], r0);
-    r1 = dot2_bf16_ones(pw[2 * g + 1], r1);
+    if (g == 0) {
+      // The first terms start from an inline zero (VOP3P form) instead of a
+      // zeroed register, which the accumulating VOP2 form the builtin
+      // selects would need: two moves fewer per phase, same arithmetic.
+      asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r0) : "v"(pw[0]), "s"(0x3F803F80u));
+      asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r1) : "v"(pw[1]), "s"(0x3F803F80u));
+    } else {
+      r0 = dot2_bf16_ones(pw[2 * g], r0);
+      r1 = dot2_bf16_ones(pw[2 * g + 1], r1);
+    }
   };
   // V^T operand of one O^T MFMA: head-dim block db, 16-key step kl of the
   // half tile in block blk of stage st.
@@ -254,6 +263,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       pend *= alpha;
+      owed = true;
       l_run *= alpha;
       m_run = m_new;
       float r0 = 0.f, r1 = 0.f;
@@ -263,6 +273,20 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
       rs = r0 + r1;
     }
     l_run += rs;
+  };
+  // P of a wave's first half tile: the offset is still -inf and O and l are
+  // zero, so the exact row maximum is taken at once (no rescale is owed)
+  // instead of computing P with the running offset first.
+  auto first_p = [&](const f32x16& s, uint32_t (&pw)[8]) __attribute__((always_inline)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    m_run = xhalf_max(mx) * c;
+    const float m = m_run == -INFINITY ? 0.f : m_run;
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) p_chunk(s, m, g, pw, r0, r1);
+    l_run = r0 + r1;
   };
   // Causal diagonal / ragged tail mask of half tile hh.  Element e of a lane
   // is key k0 + 4*lg + (e/4)*8 + e%4; it is masked when that key exceeds the
@@ -278,12 +302,13 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
       if ((e >> 2) * 8 + (e & 3) > d) s[e] = -INFINITY;
   };
   auto apply_rescale = [&]() __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(pend != 1.f) != 0) {
+    if (owed) {
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= pend;
       pend = 1.f;
+      owed = false;
     }
   };
 
@@ -322,10 +347,11 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
     } else {
       k0 = read_k(ss, 1 - blk, 0);
       k1 = read_k(ss, 1 - blk, 1);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) p_chunk(s, m_run, g, pcur, r0, r1);
     }
-    finish_p(s, r0 + r1, pcur);
+    if (hh > 0)
+      finish_p(s, r0 + r1, pcur);
+    else
+      first_p(s, pcur);
     if (hh + 1 < nh) mfma_s(ss, 1 - blk, k0, k1, s);
   };
 
