@@ -138,11 +138,12 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const BwdFinalizeArgs
 // skipped by whole workgroups and each lane loads only the kept partials.
 // A workgroup sums one of the three gradients; the patterns go in groups of
 // four whose loads issue before the group's adds (which keep descriptor
-// order).  Grid: (row blocks, R, 3*B*H).
+// order).  Grid: (row blocks, R / cls_step, 3*B*H): when cls_step > 1 the
+// classes that only the r = 1 pattern keeps are not launched.
 __global__ __launch_bounds__(256) void bwd_finalize_class_kernel(const BwdFinalizeArgs a) {
   const uint32_t g = blockIdx.z % 3u, bhu = blockIdx.z / 3u;
   const uint32_t h = bhu % (uint32_t)a.H, b = bhu / (uint32_t)a.H;
-  const uint32_t rho = blockIdx.y;
+  const uint32_t rho = h % a.cls_step + a.cls_step * blockIdx.y;
   uint32_t kept = 0;
   for (int p = 0; p < a.P; ++p) {
     const uint32_t rp = (uint32_t)a.r[p];
@@ -193,7 +194,7 @@ hipError_t launch_bwd_finalize(const BwdFinalizeArgs& a, hipStream_t stream) {
   if (a.B * a.N * a.H == 0) return hipSuccess;
   TimedLaunch tl("bwd_finalize", stream);
   if (a.R && 3 * a.B * a.H <= 65535) {
-    const dim3 g((a.rows_per_class + 31) / 32, a.R, (unsigned)(3 * a.B * a.H));
+    const dim3 g((a.rows_per_class + 31) / 32, a.R / a.cls_step, (unsigned)(3 * a.B * a.H));
     hipLaunchKernelGGL(bwd_finalize_class_kernel, g, dim3(256), 0, stream, a);
   } else {
     const dim3 grid((unsigned)(a.B * a.nblk), (unsigned)a.H);

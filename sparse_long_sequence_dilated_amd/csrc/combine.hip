@@ -148,12 +148,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
 // rows n = rho + R*t of one class rho and one (batch, head) has one kept set
 // for all its lanes: rows only the primary pattern keeps are skipped by whole
 // workgroups, and each lane loads exactly the kept patterns' rows, with no
-// divergence and no discarded loads.  Grid: (row blocks, R, B*H).
+// divergence and no discarded loads.  Grid: (row blocks, R / cls_step, B*H):
+// when cls_step > 1 the classes that only the primary pattern keeps are not
+// launched at all (half of the workgroups with geometric rates).
 template <typename T, int NP>
 __global__ __launch_bounds__(256) void combine_class_kernel(const CombineArgs a) {
   const uint32_t bhu = blockIdx.z;
   const uint32_t h = bhu % (uint32_t)a.H, b = bhu / (uint32_t)a.H;
-  const uint32_t rho = blockIdx.y;
+  const uint32_t rho = h % a.cls_step + a.cls_step * blockIdx.y;
   uint32_t kept = 0;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256) void combine_class_kernel(const CombineArgs a)
 template <typename T>
 static void launch_combine_np(const CombineArgs& a, dim3 grid, hipStream_t stream) {
   if (a.R) {
-    const dim3 g((a.rows_per_class + 31) / 32, a.R, (unsigned)(a.B * a.H));
+    const dim3 g((a.rows_per_class + 31) / 32, a.R / a.cls_step, (unsigned)(a.B * a.H));
     switch (a.P) {
 #define DLA_COMBINE_CASE(np) \
       case np: hipLaunchKernelGGL((combine_class_kernel<T, np>), g, dim3(256), 0, stream, a); break;

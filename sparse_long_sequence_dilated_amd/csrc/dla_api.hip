@@ -121,9 +121,12 @@ static int forward_impl(const Plan& pl, const void* q, const void* k, const void
     }
     const int64_t rpc = R <= pl.N ? pl.N / R : 0;
     cb.R = 0;
+    cb.cls_step = 1;
     if (rpc >= 32 && R <= 65535 && pl.B * pl.H <= 65535 && R * (int64_t)rpc == pl.N) {
       cb.R = (uint32_t)R;
       cb.rows_per_class = (uint32_t)rpc;
+      // Only the classes that another pattern than the primary keeps.
+      if (pl.r[pl.prim] == 1) cb.cls_step = class_step(pl);
     }
     if (pl.need_combine) {
       e = launch_combine(cb, pl.dtype, st);

@@ -140,6 +140,7 @@ static int run_finalize(const Plan& pl, char* wsb, void* dq, void* dk, void* dv,
   f.nblk = (uint32_t)((pl.N + 31) / 32);
   f.span_mask = pl.span_mask;
   residue_classes(pl, &f.R, &f.rows_per_class);
+  f.cls_step = f.R ? class_step(pl) : 1u;  // classes kept by two or more patterns
   hipError_t e = launch_bwd_finalize(f, st);
   if (e != hipSuccess) return hip_fail(e, "backward finalize launch");
   return DLA_OK;

@@ -60,6 +60,11 @@ struct CombineArgs {
   // rates share the set of patterns that keep them.
   uint32_t R;              // 0: per-row launch
   uint32_t rows_per_class; // N / R
+  // Classes that only the primary pattern keeps are not launched when every
+  // class another pattern keeps satisfies rho = h mod cls_step (grid.y is
+  // then R / cls_step and rho = h mod cls_step + cls_step * blockIdx.y);
+  // cls_step = 1 launches every class.
+  uint32_t cls_step;
   const int32_t* lengths;  // per-batch sequence lengths (device), null: all N
 };
 
@@ -152,6 +157,7 @@ struct BwdFinalizeArgs {
   uint32_t nblk;           // row blocks of 32 per (batch, head)
   uint32_t R;              // residue-class launch: R = lcm of the rates (0: per row)
   uint32_t rows_per_class; // N / R
+  uint32_t cls_step;       // classes launched: rho = h mod cls_step + cls_step * blockIdx.y
   uint32_t span_mask;      // sequence shard: patterns whose segments span devices
   const int32_t* lengths;  // per-batch sequence lengths (device), null: all N
 };

@@ -87,6 +87,15 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan,
 // Fill `s` for tiles of `tile_rows` sparse rows per unit.
 void make_schedule(const Plan& plan, int tile_rows, Schedule* s);
 
+// Residue classes rho (mod the lcm of the rates) that the merge passes must
+// visit for head h.  When exactly one pattern has r = 1 (and its segments
+// stay on this device) and every rate is a power of two, a row that any
+// other pattern keeps has rho = h mod r_min, r_min being the smallest other
+// rate (it divides the others); rows of the other classes are kept by the
+// r = 1 pattern alone and need no merge.  Returns r_min then, else 1 (every
+// class).
+uint32_t class_step(const Plan& plan);
+
 // Record a formatted message for dla_last_error() and return `code`.
 int fail(int code, const char* fmt, ...);
 void clear_error();
