@@ -73,6 +73,24 @@ def test_backward_small_cases(case):
             assert np.all(to_host(g)[:, ~kept, h] == 0.0)
 
 
+@pytest.mark.parametrize("case", [
+    (1, 1024, 3, ((64, 1), (128, 2), (256, 4), (512, 8), (1024, 16), (96, 3), (192, 6), (64, 2),
+                  (128, 4), (256, 8), (32, 1), (512, 4), (1024, 2), (768, 3), (384, 12), (1024, 1))),
+    (1, 2048, 2, ((64, 1), (128, 2), (256, 4), (512, 8), (1024, 16), (128, 4), (256, 2), (512, 16),
+                  (1024, 8), (256, 8), (512, 2), (1024, 4), (128, 8), (256, 16), (512, 32), (1024, 32))),
+], ids=["mixed_rates", "pow2_rates"])
+def test_backward_sixteen_patterns(case):
+    """The largest descriptor (16 patterns): per-row and residue-class finalize."""
+    B, N, H, pats = case
+    assert len(pats) == dla.MAX_PATTERNS
+    print(f"case {case}", flush=True)
+    q, k, v, do = inputs.random_case(zlib.crc32(repr(case).encode()) & 0xFFFF, B, N, H, "bf16", 4)
+    errs, _, _ = _run(q, k, v, do, pats, True, 0.125)
+    print(errs, flush=True)
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
+
+
 def test_backward_c5_full_tensor():
     import torch
     wl = inputs.WORKLOADS["C5"]

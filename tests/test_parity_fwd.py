@@ -72,6 +72,27 @@ def test_forward_small_cases(case):
     _check_forward(q, k, v, pats, causal, 0.125, dtype, layout)
 
 
+# The largest descriptor the ABI takes: 16 patterns.  The first mixes rates
+# 3, 6 and 12 with powers of two (lcm 48 does not divide N: per-row merge)
+# and cuts segments short; the second uses powers of two only (residue-class
+# merge, only the classes another pattern keeps launched).
+SIXTEEN = [
+    (1, 1024, 3, ((64, 1), (128, 2), (256, 4), (512, 8), (1024, 16), (96, 3), (192, 6), (64, 2),
+                  (128, 4), (256, 8), (32, 1), (512, 4), (1024, 2), (768, 3), (384, 12), (1024, 1))),
+    (1, 2048, 2, ((64, 1), (128, 2), (256, 4), (512, 8), (1024, 16), (128, 4), (256, 2), (512, 16),
+                  (1024, 8), (256, 8), (512, 2), (1024, 4), (128, 8), (256, 16), (512, 32), (1024, 32))),
+]
+
+
+@pytest.mark.parametrize("case", SIXTEEN, ids=["mixed_rates", "pow2_rates"])
+def test_forward_sixteen_patterns(case):
+    B, N, H, pats = case
+    assert len(pats) == dla.MAX_PATTERNS
+    print(f"case {case}", flush=True)
+    q, k, v = inputs.random_case(zlib.crc32(repr(case).encode()) & 0xFFFF, B, N, H, "bf16")
+    _check_forward(q, k, v, pats, True, 0.125, "bf16")
+
+
 def test_forward_empty_batch():
     import torch
     q = torch.empty((0, 256, 2, 64), dtype=torch.bfloat16, device="cuda")
