@@ -34,6 +34,10 @@ SMALL = [
     (1, 1000, 3, ((256, 1), (512, 2), (2048, 4)), False, "bnhd"),
     (1, 602, 5, ((300, 4), (640, 1)), True, "bhnd"),               # heads 2, 3: last segment empty
     (1, 1000, 2, ((4096, 1),), True, "bnhd"),
+    # residue-class finalize where every class must be launched: two patterns
+    # of rate 1, or none (rows left uncovered)
+    (1, 2048, 3, ((128, 1), (256, 1), (512, 2), (1024, 4)), True, "bnhd"),
+    (1, 2048, 3, ((256, 2), (512, 4), (1024, 8)), True, "bnhd"),
 ]
 
 

@@ -45,6 +45,10 @@ SMALL = [
     (1, 1000, 2, ((4096, 1),), True, "bf16", "bnhd"),                # one segment shorter than w
     (2, 500, 3, ((128, 1), (256, 2), (1024, 4)), True, "f32", "bnhd"),
     (1, 500, 3, ((200, 4), (1024, 1)), False, "f32", "bnhd"),
+    # residue-class merge where every class must be launched: two patterns of
+    # rate 1, or none (rows left uncovered)
+    (1, 2048, 3, ((128, 1), (256, 1), (512, 2), (1024, 4)), True, "bf16", "bnhd"),
+    (1, 2048, 3, ((256, 2), (512, 4), (1024, 8)), True, "bf16", "bnhd"),
 ]
 
 
