@@ -9,7 +9,9 @@ patterns w = 2048*2^i, r = 2^i for i = 0..4 (the 768-dim, 12-head model
 settings of the gptget.net LongNet summary, section 实验设计, at 32K tokens).
 
 Also reported, as extra fields of the same line:
-  * forward-only throughput at N=32768 (B=1) and N=1,048,576 (B=1);
+  * forward-only throughput of every forward workload: fp32 N=2048 (B=1,
+    non-causal, on the vector ALUs, also against the fp32 peak), bf16
+    N=8192 (B=4), N=32768 (B=1) and N=1,048,576 (B=1);
   * `shard_forward`: one device's share when the 1M-token sequence is split
     over 8 devices (the last shard, whose segments of the three coarsest
     patterns span 2, 4 and 8 devices): its exchange parts and its forward,
@@ -23,6 +25,8 @@ Also reported, as extra fields of the same line:
     last-level cache (`value` is the warm, back-to-back step);
   * `roofline` of the kernel family that takes most of the timed region,
     timed live with HIP events around its launches on the launch stream;
+  * `ms_per_step_no_events`: the same steps again with the launch timing
+    off, which shows what the HIP events cost;
   * `cpu_baseline`: the CPU oracle (float32, thread pool) on a bounded
     sample of the same workload, scaled to the full workload.
 
@@ -44,8 +48,11 @@ if ROOT not in sys.path:
 
 METRIC = "tokens/s and % of bf16 MFMA peak, dilated attn fwd(+bwd), N=32K & 1M, 1 GPU"
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3      # MI355X fp32 vector (the fp32 forward runs on the VALU)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+FAMILIES = ("attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "combine", "bwd_prep", "attn_bwd",
+            "bwd_finalize", "shard_gather", "shard_finish", "quantize_fp8")
 KERNEL_SOURCES = {
     "attn_fwd": ["attn_fwd_bf16.hip", "dla_device.h"],
     "attn_bwd": ["attn_bwd_bf16.hip", "dla_device.h"],
@@ -67,7 +74,8 @@ def gpu_inputs(wl, count, seed):
     import torch
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
-    return [torch.randn((wl.B, wl.N, wl.H, wl.D), device="cuda", generator=g).bfloat16()
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    return [torch.randn((wl.B, wl.N, wl.H, wl.D), device="cuda", generator=g).to(dt)
             for _ in range(count)]
 
 
@@ -121,10 +129,21 @@ def traffic_for(family, launches_per_step):
 
 
 def time_steps(step, steps, warmup):
+    """Wall time per step over `steps` timed steps (after `warmup`), with each
+    library launch bracketed by HIP events on its stream; returns
+    (ms per step, {family: (launches, total ms)})."""
     import torch
     from sparse_long_sequence_dilated_amd import dla
     for _ in range(warmup):
         step()
+    torch.cuda.synchronize()
+    # fill the library's event pool so the timed steps create no events
+    dla.timing_enable(True)
+    step()
+    torch.cuda.synchronize()
+    dla.timing_enable(False)
+    for fam in FAMILIES:
+        dla.timing_collect(fam)
     torch.cuda.synchronize()
     dla.timing_enable(True)
     t0 = time.perf_counter()
@@ -134,12 +153,22 @@ def time_steps(step, steps, warmup):
     t1 = time.perf_counter()
     dla.timing_enable(False)
     fams = {}
-    for fam in ("attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "combine", "bwd_prep", "attn_bwd",
-                "bwd_finalize", "shard_gather", "shard_finish", "quantize_fp8"):
+    for fam in FAMILIES:
         n, ms = dla.timing_collect(fam)
         if n:
             fams[fam] = (n, ms)
     return (t1 - t0) * 1e3 / steps, fams
+
+
+def time_steps_plain(step, steps):
+    """Wall time per step with the launch timing off (no events recorded)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def cold_kernel_ms(step, steps, flush_bytes=512 << 20):
@@ -159,8 +188,7 @@ def cold_kernel_ms(step, steps, flush_bytes=512 << 20):
         step()
         torch.cuda.synchronize()
         dla.timing_enable(False)
-        for fam in ("attn_fwd", "attn_fwd_f32", "attn_fwd_fp8", "combine", "bwd_prep", "attn_bwd",
-                    "bwd_finalize", "shard_gather", "shard_finish", "quantize_fp8"):
+        for fam in FAMILIES:
             total += dla.timing_collect(fam)[1]
     del buf
     return total / steps
@@ -171,7 +199,8 @@ def forward_only(name, steps, warmup):
     from sparse_long_sequence_dilated_amd import dla, inputs
     wl = inputs.WORKLOADS[name]
     q, k, v = gpu_inputs(wl, 3, 1000 + wl.seed)
-    ws_f, _ = dla.plan_check(wl.patterns, wl.causal, wl.scale, wl.B, wl.N, wl.H)
+    dt = dla.DLA_F32 if wl.dtype == "f32" else dla.DLA_BF16
+    ws_f, _ = dla.plan_check(wl.patterns, wl.causal, wl.scale, wl.B, wl.N, wl.H, dtype=dt)
     ws = torch.empty(max(ws_f, 1), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device="cuda")
@@ -184,8 +213,15 @@ def forward_only(name, steps, warmup):
     tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
     out = {"workload": wl.describe(), "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "ms": ms,
            "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS}
+    if wl.dtype == "f32":
+        # fp32 runs on the vector ALUs: its own peak is the one that bounds it
+        out["pct_fp32_peak"] = 100.0 * tflops / FP32_PEAK_TFLOPS
     for fam, (n, fms) in fams.items():
         out[f"{fam}_us_per_launch"] = 1e3 * fms / n
+        if fam in ("attn_fwd", "attn_fwd_f32"):
+            kt = 4 * wl.D * pairs / (fms * 1e-3 / n) / 1e12
+            out[f"{fam}_tflops"] = kt
+            out[f"{fam}_frac_of_peak"] = kt / (FP32_PEAK_TFLOPS if fam == "attn_fwd_f32" else BF16_PEAK_TFLOPS)
     cold = cold_kernel_ms(step, min(steps, 10))
     out["cold_cache"] = {"kernel_ms": cold, "tokens_per_s": wl.B * wl.N / (cold * 1e-3),
                          "pct_bf16_peak": 100.0 * 4 * wl.D * pairs / (cold * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
@@ -295,14 +331,28 @@ def shard_forward(name, devices, shard, steps, warmup):
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, min_seconds=10.0, max_passes=30):
     """The oracle (float32, thread pool) on batch 0 of the workload, all heads,
-    repeated until about `min_seconds` of CPU work have run."""
+    repeated until about `min_seconds` of CPU work have run.  One worker per
+    CPU this process may run on, at most 16 (one GPU's share of the host)."""
     import numpy as np
 
     import oracle
     from sparse_long_sequence_dilated_amd import inputs
-    workers = max(1, min(16, os.cpu_count() or 1))
+    host_cpus = os.cpu_count() or 1
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else host_cpus
+    workers = max(1, min(16, usable))
     q, k, v, do = inputs.draw((1, wl.N, wl.H, wl.D), wl.seed, 4, wl.dtype)
     passes, t = 0, 0.0
     while passes < max_passes and (passes == 0 or t < min_seconds):
@@ -316,10 +366,13 @@ def cpu_baseline(wl, min_seconds=10.0, max_passes=30):
         passes += 1
     per_pass = t / passes
     return {"value": wl.B * wl.N / (per_pass * wl.B), "unit": "tokens/s", "cores": workers,
-            "kind": "oracle",
+            "kind": "oracle", "threads": workers, "host_cpus": host_cpus, "usable_cpus": usable,
+            "cpu_model": cpu_model(),
             "sample": (f"{'fwd+bwd' if wl.backward else 'fwd'} of batch 1 of {wl.B} (all {wl.H} heads, "
                        f"full N={wl.N}, all patterns), {passes} passes in {t:.1f} s; float32 NumPy "
-                       f"oracle, {workers} threads; scaled by {wl.B} to the full batch")}
+                       f"oracle, one worker thread per usable CPU up to 16 ({workers} of "
+                       f"{usable} usable, {host_cpus} on the host), BLAS at 1 thread each; "
+                       f"scaled by {wl.B} to the full batch")}
 
 
 def layer_bench(B, N, steps, warmup):
@@ -425,6 +478,7 @@ def main():
                          dv=dv, workspace=ws_bwd)
 
     ms, fams = time_steps(step, args.steps, args.warmup)
+    ms_plain = time_steps_plain(step, args.steps)
     pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
     flops = (14 if wl.backward else 4) * wl.D * pairs
     tflops = flops / (ms * 1e-3) / 1e12
@@ -451,6 +505,8 @@ def main():
 
     extra = []
     if not args.no_forward_lines:
+        extra.append(forward_only("C1", max(5, args.steps), args.warmup))
+        extra.append(forward_only("C2", max(5, args.steps), args.warmup))
         extra.append(forward_only("C3", max(5, args.steps), args.warmup))
         extra.append(forward_only("C4", max(3, args.steps // 4), 1))
         extra.append(fp8_forward("C3", max(5, args.steps), args.warmup))
@@ -467,6 +523,7 @@ def main():
                    "patterns": [list(p) for p in wl.patterns], "causal": wl.causal,
                    "step": "dla_forward + dla_backward" if wl.backward else "dla_forward"},
         "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        "ms_per_step_no_events": ms_plain,
         "roofline": roofline, "kernels": kernels, "forward_only": extra, "cpu_baseline": cpu,
         "cold_cache": {"kernel_ms_per_step": cold, "tokens_per_s": wl.B * wl.N / (cold * 1e-3),
                        "note": "512 MB written between steps; kernel time only"},

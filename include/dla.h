@@ -36,7 +36,10 @@
  *   - The caller owns every buffer, including the workspace; the library
  *     allocates and frees no device memory, keeps no device state and never
  *     synchronises (apart from dla_timing_collect, which waits for its
- *     events).  The exceptions are the attention layer's calls:
+ *     events).  Its only global state is the opt-in timing record of
+ *     dla_timing_enable (host memory: a flag, the recorded events and a
+ *     pool of reusable events, behind a mutex) and the thread-local error
+ *     text.  The exceptions are the attention layer's calls:
  *     dla_blas_create makes a hipBLASLt handle (its own host and device
  *     state), and each layer call creates and destroys hipBLASLt's small
  *     host-side descriptors.  Work is enqueued on `stream` (a hipStream_t;
@@ -364,12 +367,16 @@ int dla_layer_backward(const dla_desc* desc, int64_t B, int64_t N, int64_t H, co
 
 /*
  * Opt-in launch timing, a profiling aid.  While enabled (on != 0), every
- * kernel launch made by dla_forward / dla_backward is bracketed by two HIP
- * events recorded on the caller's stream (host-side bookkeeping only; the
- * kernels are unchanged).  Kernel families: "attn_fwd" (bf16 forward
- * attention), "attn_fwd_f32", "combine", "bwd_prep", "attn_bwd",
- * "bwd_finalize", "shard_gather" (a shard's exchange parts and
- * relayouts), "shard_finish".
+ * kernel launch made by the library is bracketed by two HIP events recorded
+ * on the caller's stream (host-side bookkeeping only; the kernels are
+ * unchanged).  This record is process-wide: the one global state of the
+ * library besides the thread-local error text.  Events are taken from a
+ * pool that dla_timing_collect refills, so a timed launch creates no event
+ * once the pool holds as many as are in flight.  Kernel families:
+ * "attn_fwd" (bf16 forward attention), "attn_fwd_f32", "attn_fwd_fp8" (8-bit
+ * keys and values), "combine", "bwd_prep", "attn_bwd", "bwd_finalize",
+ * "shard_gather" (a shard's exchange parts and relayouts), "shard_finish",
+ * "quantize_fp8".
  */
 int dla_timing_enable(int on);
 

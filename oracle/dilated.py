@@ -139,31 +139,38 @@ def _lengths(lengths, B, N):
     return [N] * B if lengths is None else [int(x) for x in lengths]
 
 
-def forward(q, k, v, patterns, causal, scale, dtype=np.float64, workers=1, lengths=None):
+def forward(q, k, v, patterns, causal, scale, dtype=np.float64, workers=1, lengths=None,
+            heads=None):
     """Dilated attention forward; returns (O [B,N,H,D], LSE [B,H,N]).
 
     An explicit loop over pattern, batch, head and segment: gather the rows the
     pattern keeps, attend densely inside the segment, scatter the result back
     into a per-pattern buffer (rows a pattern does not select keep O_p = 0,
     LSE_p = -inf), then merge the patterns with `combine`.  With `lengths`,
-    batch b's sequence is its first lengths[b] rows.
+    batch b's sequence is its first lengths[b] rows.  `heads` names the head
+    index of each entry of the inputs' head axis (default 0..H-1), so that a
+    slice q[:, :, h:h+1] with heads=[h] gives head h's result alone (the head
+    index sets the row offset h mod r).
     """
     q, k, v = (np.asarray(t, dtype=dtype) for t in (q, k, v))
     B, N, H, D = q.shape
     check_patterns(N, patterns)
     lens = _lengths(lengths, B, N)
+    head_ids = list(range(H)) if heads is None else [int(x) for x in heads]
+    if len(head_ids) != H:
+        raise ValueError(f"heads names {len(head_ids)} heads for an input with {H}")
     o_parts = [np.zeros((B, N, H, D), dtype) for _ in patterns]
     lse_parts = [np.full((B, H, N), -np.inf, dtype) for _ in patterns]
 
     def unit(u):
-        p, b, h, s = u
+        p, b, j, s = u          # j: position on the inputs' head axis
         w, r = patterns[p]
-        idx = segment_rows(lens[b], w, r, h, s)
+        idx = segment_rows(lens[b], w, r, head_ids[j], s)
         if idx.size == 0:
             return
-        o, lse = segment_attention(q[b, idx, h], k[b, idx, h], v[b, idx, h], scale, causal)
-        o_parts[p][b, idx, h] = o
-        lse_parts[p][b, h, idx] = lse
+        o, lse = segment_attention(q[b, idx, j], k[b, idx, j], v[b, idx, j], scale, causal)
+        o_parts[p][b, idx, j] = o
+        lse_parts[p][b, j, idx] = lse
 
     _run(_units(patterns, B, H, N), unit, workers)
     o, lse = combine(o_parts, [x.transpose(0, 2, 1) for x in lse_parts])
@@ -347,7 +354,3 @@ def pair_count(B, N, H, patterns, causal, lengths=None):
                     total += L * (L + 1) // 2 if causal else L * L
     return total
 
-
-def useful_flops(B, N, H, D, patterns, causal, with_backward=False):
-    """Algorithmic FLOPs: 4*D per pair forward (QK^T and PV), plus 10*D for the backward."""
-    return (14 if with_backward else 4) * D * pair_count(B, N, H, patterns, causal)

@@ -162,6 +162,15 @@ def _same_layout(ref, *ts):
             raise DlaError(DLA_E_INVALID, "all tensors must be on one device")
 
 
+def _check_lse(lse, q):
+    """lse must be a contiguous float32 [B, H, N] tensor on q's device."""
+    import torch
+    B, N, H, _ = q.shape
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or not lse.is_contiguous()
+            or lse.dtype != torch.float32 or lse.device != q.device):
+        raise DlaError(DLA_E_INVALID, "lse must be a contiguous float32 [B, H, N] tensor on q's device")
+
+
 def _stream(stream, device):
     import torch
     if stream is None:
@@ -215,8 +224,7 @@ def forward(q, k, v, patterns, causal=True, scale=None, out=None, lse=None, work
     o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
     _same_layout(q, o)
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    if lse_t.shape != (B, H, N) or not lse_t.is_contiguous() or lse_t.dtype != torch.float32:
-        raise DlaError(DLA_E_INVALID, "lse must be a contiguous float32 [B, H, N] tensor")
+    _check_lse(lse_t, q)
     if workspace is None:
         workspace = torch.empty(max(ws_f.value, 1), dtype=torch.uint8, device=q.device)
     _check(lib().dla_forward(ctypes.byref(desc), ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
@@ -231,6 +239,7 @@ def backward(q, k, v, o, lse, dout, patterns, causal=True, scale=None, dq=None, 
     import torch
     scale = default_scale(q.shape[-1]) if scale is None else scale
     _same_layout(q, k, v, o, dout)
+    _check_lse(lse, q)
     shape = _shape_of(q)
     desc = make_desc(patterns, causal, scale)
     ws_b = ctypes.c_size_t(0)
@@ -342,8 +351,7 @@ def forward_shard(q, k, v, patterns, total_rows, shard_start, ext_k=None, ext_v=
     o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
     _same_layout(q, o)
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    if lse_t.shape != (B, H, N) or not lse_t.is_contiguous() or lse_t.dtype != torch.float32:
-        raise DlaError(DLA_E_INVALID, "lse must be a contiguous float32 [B, H, N] tensor")
+    _check_lse(lse_t, q)
     P = len(patterns)
     ek = (ctypes.c_void_p * P)()
     ev = (ctypes.c_void_p * P)()
@@ -384,6 +392,7 @@ def backward_shard(q, k, v, o, lse, dout, patterns, total_rows, shard_start, ext
     import torch
     scale = default_scale(q.shape[-1]) if scale is None else scale
     _same_layout(q, k, v, o, dout)
+    _check_lse(lse, q)
     shape = _shape_of(q)
     desc = make_desc(patterns, causal, scale)
     sh = Shard(total_rows, shard_start)
@@ -456,6 +465,7 @@ def forward_varlen(q, k, v, lengths, patterns, causal=True, scale=None, out=None
     o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
     _same_layout(q, o)
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_lse(lse_t, q)
     if workspace is None:
         workspace = torch.empty(max(ws_f.value, 1), dtype=torch.uint8, device=q.device)
     _check(lib().dla_forward_varlen(ctypes.byref(desc), ctypes.byref(shape), lt.data_ptr(), q.data_ptr(),
@@ -470,6 +480,7 @@ def backward_varlen(q, k, v, o, lse, dout, lengths, patterns, causal=True, scale
     import torch
     scale = default_scale(q.shape[-1]) if scale is None else scale
     _same_layout(q, k, v, o, dout)
+    _check_lse(lse, q)
     shape = _shape_of(q)
     desc = make_desc(patterns, causal, scale)
     ws_b = ctypes.c_size_t(0)
@@ -611,6 +622,7 @@ def forward_fp8kv(q, k8, v8, k_scale, v_scale, patterns, causal=True, scale=None
     o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
     _same_layout(q, o)
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_lse(lse_t, q)
     if workspace is None:
         workspace = torch.empty(max(ws_f.value, 1), dtype=torch.uint8, device=q.device)
     _check(lib().dla_forward_fp8kv(ctypes.byref(desc), ctypes.byref(shape), q.data_ptr(), k8.data_ptr(),

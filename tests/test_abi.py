@@ -262,3 +262,24 @@ def test_fp8_entry_points_reject_bad_arguments_before_any_launch():
                                16, 1 << 20, None) == dla.DLA_E_UNSUPPORTED
     assert L.dla_forward_fp8kv(ctypes.byref(desc), ctypes.byref(ok), 16, 16, 16, None, 16, 16, 16,
                                16, 1 << 20, None) == dla.DLA_E_INVALID
+
+
+@pytest.mark.parametrize("bad", ["bf16", "bnh", "strided", "shape"])
+def test_backward_entry_points_reject_a_bad_lse_before_any_launch(bad):
+    """The backward reads lse as a contiguous float32 [B, H, N] array: any
+    other dtype, layout or shape is refused by the binding, on the host."""
+    import torch
+    B, N, H = 1, 256, 2
+    x = torch.zeros((B, N, H, 64), dtype=torch.bfloat16)
+    lse = {"bf16": torch.zeros((B, H, N), dtype=torch.bfloat16),
+           "bnh": torch.zeros((B, N, H), dtype=torch.float32),
+           "strided": torch.zeros((B, N, H), dtype=torch.float32).permute(0, 2, 1),
+           "shape": torch.zeros((B, H, N + 1), dtype=torch.float32)}[bad]
+    calls = [lambda: dla.backward(x, x, x, x, lse, x, [(64, 1)], True),
+             lambda: dla.backward_varlen(x, x, x, x, lse, x, [N], [(64, 1)], True),
+             lambda: dla.backward_shard(x, x, x, x, lse, x, [(64, 1)], 2 * N, 0)]
+    for call in calls:
+        with pytest.raises(dla.DlaError) as ei:
+            call()
+        assert ei.value.code == dla.DLA_E_INVALID
+        assert "lse" in str(ei.value)

@@ -179,6 +179,24 @@ def test_forward_rows_matches_forward():
             np.testing.assert_allclose(lrow, lse[b, h, rows], rtol=1e-12, atol=1e-12)
 
 
+def test_single_head_slices_match_the_brute_force_heads():
+    """forward on one head's slice, with `heads` naming that head, gives the
+    head's result: its row offsets follow the named head (h mod r), checked
+    against the union-softmax brute force on all heads (rates 3 and 4 make
+    every head's offset set differ)."""
+    q, k, v = _rand(31, 2, 96, 5, 8)
+    pats = [(12, 1), (24, 3), (48, 4), (96, 12)]
+    ob, lb = oracle.brute_force_forward(q, k, v, pats, True, 0.3)
+    for h in range(5):
+        sl = slice(h, h + 1)
+        o, lse = oracle.forward(q[:, :, sl], k[:, :, sl], v[:, :, sl], pats, True, 0.3, heads=[h],
+                                workers=2)
+        np.testing.assert_allclose(o[:, :, 0], ob[:, :, h], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[:, 0], lb[:, h], rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.forward(q, k, v, pats, True, 0.3, heads=[0])
+
+
 def test_float32_and_threaded_paths_agree_with_float64():
     wl = inputs.WORKLOADS["C1"]
     q, k, v = inputs.draw((1, 512, 4, 64), 1, 3, "f32")

@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 from sparse_long_sequence_dilated_amd import dla, inputs
-from tests.gpu_util import ORACLE_WORKERS, TOL, nan_like, normwise, to_device, to_host
+from tests.gpu_util import (ORACLE_WORKERS, TOL, check_fwd, check_grads, nan_like, nan_lse, normwise, to_device,
+                            to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,16 +45,17 @@ SMALL = [
 def _run(q, k, v, do, pats, causal, scale, layout="bnhd", workers=1, ref_dtype=np.float64):
     import torch
     tq, tk, tv, tdo = (to_device(x, "bf16", layout) for x in (q, k, v, do))
-    o, lse = dla.forward(tq, tk, tv, pats, causal, scale)
+    o, lse = nan_like(tq), nan_lse(tq)
+    dla.forward(tq, tk, tv, pats, causal, scale, out=o, lse=lse)
     dq, dk, dv = nan_like(tq), nan_like(tq), nan_like(tq)
     dla.backward(tq, tk, tv, o, lse, tdo, pats, causal, scale, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, scale, dtype=ref_dtype, workers=workers)
     refs = oracle.backward(q, k, v, o_ref, lse_ref, do, pats, causal, scale, dtype=ref_dtype,
                            workers=workers)
-    errs = {}
-    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
-        errs[name] = normwise(to_host(got), ref)
+    # the forward outputs the backward consumes, then the gradients
+    check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "forward:")
+    errs = check_grads([to_host(g) for g in (dq, dk, dv)], refs, "backward:")
     return errs, (dq, dk, dv), refs
 
 
@@ -64,9 +66,6 @@ def test_backward_small_cases(case):
     print(f"case {case}", flush=True)
     q, k, v, do = inputs.random_case(zlib.crc32(repr(case).encode()) & 0xFFFF, B, N, H, "bf16", 4)
     errs, got, refs = _run(q, k, v, do, pats, causal, 0.125, layout)
-    print(errs, flush=True)
-    for name, e in errs.items():
-        assert e <= TOL["bf16"], (name, e)
     # rows that no pattern keeps have exactly zero gradient
     n = np.arange(N)
     for h in range(H):
@@ -89,10 +88,7 @@ def test_backward_sixteen_patterns(case):
     assert len(pats) == dla.MAX_PATTERNS
     print(f"case {case}", flush=True)
     q, k, v, do = inputs.random_case(zlib.crc32(repr(case).encode()) & 0xFFFF, B, N, H, "bf16", 4)
-    errs, _, _ = _run(q, k, v, do, pats, True, 0.125)
-    print(errs, flush=True)
-    for name, e in errs.items():
-        assert e <= TOL["bf16"], (name, e)
+    _run(q, k, v, do, pats, True, 0.125)
 
 
 def test_backward_c5_full_tensor():
@@ -100,11 +96,8 @@ def test_backward_c5_full_tensor():
     wl = inputs.WORKLOADS["C5"]
     print(wl.describe(), flush=True)
     q, k, v, do = inputs.workload_inputs(wl)
-    errs, got, _ = _run(q, k, v, do, wl.patterns, True, wl.scale, workers=ORACLE_WORKERS,
-                        ref_dtype=np.float32)
-    print(f"C5: {errs}", flush=True)
-    for name, e in errs.items():
-        assert e <= TOL["bf16"], (name, e)
+    _, got, _ = _run(q, k, v, do, wl.patterns, True, wl.scale, workers=ORACLE_WORKERS,
+                     ref_dtype=np.float32)
     # run-to-run determinism (no atomics anywhere)
     tq, tk, tv, tdo = (to_device(x, "bf16") for x in (q, k, v, do))
     o, lse = dla.forward(tq, tk, tv, wl.patterns, True)

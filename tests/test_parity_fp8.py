@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from sparse_long_sequence_dilated_amd import dla, inputs
-from tests.gpu_util import ORACLE_WORKERS, TOL, normwise, to_device, to_host
+from tests.gpu_util import ORACLE_WORKERS, check_fwd, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -67,9 +67,7 @@ def test_forward_fp8kv_matches_oracle(case):
     vc, vsc = oracle.quantize_per_head(v)
     kd, vd = oracle.dequantize_per_head(kc, ksc), oracle.dequantize_per_head(vc, vsc)
     o_ref, lse_ref = oracle.forward(q, kd, vd, pats, causal, 0.125, workers=ORACLE_WORKERS)
-    eo, el = normwise(to_host(o), o_ref), normwise(to_host(lse), lse_ref)
-    print(f"{case}: O {eo:.3e} LSE {el:.3e}", flush=True)
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    eo, el = check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "bf16")
 
 
 def test_forward_fp8kv_32k_sampled():
@@ -89,9 +87,7 @@ def test_forward_fp8kv_32k_sampled():
     og, lg = to_host(o), to_host(lse)
     for h in (0, 5, 11):
         o_ref, lse_ref = oracle.forward_rows(q, kd, vd, wl.patterns, wl.causal, wl.scale, 0, h, rows)
-        eo, el = normwise(og[0, rows, h], o_ref), normwise(lg[0, h, rows], lse_ref)
-        print(f"C3 fp8 head {h}: O {eo:.3e} LSE {el:.3e}", flush=True)
-        assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+        eo, el = check_fwd(og[0, rows, h], lg[0, h, rows], o_ref, lse_ref, "bf16")
 
 
 def test_forward_fp8kv_rejects_fp32():

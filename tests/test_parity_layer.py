@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from sparse_long_sequence_dilated_amd import dla, inputs
-from tests.gpu_util import ORACLE_WORKERS, TOL, normwise, to_device, to_host
+from tests.gpu_util import LSE_ABS, ORACLE_WORKERS, TOL, lse_abs, normwise, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +60,9 @@ def test_layer_forward_backward(case, blas):
         e = normwise(to_host(got), ref)
         print(f"{case[:2]} {name}: {e:.3e}", flush=True)
         assert e <= TOL["bf16"], (name, e)
+    la = lse_abs(to_host(lse), saved[4])
+    print(f"{case[:2]} lse max abs {la:.3e} nats", flush=True)
+    assert la <= LSE_ABS["bf16"]
 
 
 def test_layer_32k_sampled(blas):

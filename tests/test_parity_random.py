@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from sparse_long_sequence_dilated_amd import dla, inputs
-from tests.gpu_util import TOL, normwise, to_device, to_host
+from tests.gpu_util import TOL, check_fwd, normwise, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -48,9 +48,7 @@ def test_random_case_against_brute_force(seed):
     dla.forward(tq, tk, tv, pats, causal, scale, out=o, lse=lse)
     torch.cuda.synchronize()
     o_bf, lse_bf = oracle.brute_force_forward(q, k, v, pats, causal, scale)
-    eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
-    print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
-    assert eo <= TOL[dtype] and el <= TOL[dtype]
+    eo, el = check_fwd(to_host(o), to_host(lse), o_bf, lse_bf, dtype)
     if dtype != "bf16":
         return
     dq, dk, dv = (torch.full_like(tq, float("nan")) for _ in range(3))
@@ -80,9 +78,7 @@ def test_random_varlen_case(seed):
     dla.backward_varlen(tq, tk, tv, o, lse, tdo, lens, pats, causal, 0.125, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     o_bf, lse_bf = oracle.brute_force_forward(q, k, v, pats, causal, 0.125, lengths=lens)
-    eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
-    print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    eo, el = check_fwd(to_host(o), to_host(lse), o_bf, lse_bf, "bf16")
     o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, 0.125, lengths=lens)
     refs = oracle.backward(q, k, v, o_ref, lse_ref, dout, pats, causal, 0.125, lengths=lens)
     for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
@@ -113,9 +109,7 @@ def test_random_fp8kv_case(seed):
     assert np.array_equal(v8.cpu().numpy(), vc) and np.array_equal(vs.cpu().numpy(), vsc)
     kd, vd = oracle.dequantize_per_head(kc, ksc), oracle.dequantize_per_head(vc, vsc)
     o_bf, lse_bf = oracle.brute_force_forward(q, kd, vd, pats, causal, 0.125)
-    eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
-    print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    eo, el = check_fwd(to_host(o), to_host(lse), o_bf, lse_bf, "bf16")
 
 
 def _large_case(seed):
@@ -148,9 +142,7 @@ def test_random_larger_case(seed):
     dla.backward(tq, tk, tv, o, lse, tdo, pats, causal, 0.125, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     o_bf, lse_bf = oracle.brute_force_forward(q, k, v, pats, causal, 0.125)
-    eo, el = normwise(to_host(o), o_bf), normwise(to_host(lse), lse_bf)
-    print(f"  O {eo:.3e} LSE {el:.3e}", flush=True)
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    eo, el = check_fwd(to_host(o), to_host(lse), o_bf, lse_bf, "bf16")
     o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, 0.125)
     refs = oracle.backward(q, k, v, o_ref, lse_ref, dout, pats, causal, 0.125)
     for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):

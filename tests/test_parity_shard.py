@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from sparse_long_sequence_dilated_amd import dla, inputs
-from tests.gpu_util import TOL, normwise, to_device, to_host
+from tests.gpu_util import TOL, check_fwd, normwise, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -103,9 +103,7 @@ def test_forward_shards_match_whole_sequence_oracle(case):
     tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
     o, lse = _run_shards(tq, tk, tv, pats, causal, 0.125, N, total)
     o_ref, lse_ref = oracle.forward(q, k, v, pats, causal, 0.125)
-    eo, el = normwise(to_host(o), o_ref), normwise(to_host(lse), lse_ref)
-    print(f"{case}: O {eo:.3e} LSE {el:.3e}", flush=True)
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    eo, el = check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "bf16")
 
 
 def test_forward_shard_c4_eight_way_last_shard_sampled_rows():
@@ -133,10 +131,8 @@ def test_forward_shard_c4_eight_way_last_shard_sampled_rows():
         local = np.unique(np.concatenate([special, rng.integers(0, N, 41)]))
         o_ref, l_ref = oracle.forward_rows(q, k, v, wl.patterns, True, wl.scale, 0, h, g * N + local)
         idx = torch.from_numpy(local).cuda()
-        eo = normwise(o[0, :, h][idx].float().cpu().numpy(), o_ref)
-        el = normwise(lse[0, h][idx].cpu().numpy(), l_ref)
-        print(f"C4 shard {g}/{G} head {h}: O {eo:.3e} LSE {el:.3e}", flush=True)
-        assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+        check_fwd(o[0, :, h][idx].float().cpu().numpy(), lse[0, h][idx].cpu().numpy(), o_ref, l_ref,
+                  "bf16", f"C4 shard {g}/{G} head {h}:")
 
 
 BWD_CASES = [
