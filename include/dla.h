@@ -38,8 +38,10 @@
  *     synchronises (apart from dla_timing_collect, which waits for its
  *     events).  Its only global state is the opt-in timing record of
  *     dla_timing_enable (host memory: a flag, the recorded events and a
- *     pool of reusable events, behind a mutex) and the thread-local error
- *     text.  The exceptions are the attention layer's calls:
+ *     pool of reusable events, behind a mutex), the thread-local error
+ *     text, and dla_forward_noalloc's static device scratch (part of the
+ *     library's code object, with its per-device addresses).  The
+ *     exceptions are the attention layer's calls:
  *     dla_blas_create makes a hipBLASLt handle (its own host and device
  *     state), and each layer call creates and destroys hipBLASLt's small
  *     host-side descriptors.  Work is enqueued on `stream` (a hipStream_t;
@@ -111,6 +113,27 @@ int dla_plan_check(const dla_desc* desc, const dla_shape* shape, size_t* ws_fwd_
  */
 int dla_forward(const dla_desc* desc, const dla_shape* shape, const void* q, const void* k,
                 const void* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dla_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels and results as dla_forward, but the workspace is a static
+ * array inside the library, DLA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU
+ * the library's code is loaded on, held until the process ends; the call
+ * allocates and frees nothing.  The scratch of the current device
+ * (hipGetDevice) is used, so `stream` must belong to that device.  Every
+ * call on one GPU shares that GPU's scratch: calls whose execution overlaps
+ * on one GPU (other streams, other threads) race and must be serialised by
+ * the caller; calls in one stream are ordered and safe.  Nothing in the
+ * scratch needs clearing between calls (each partial result is written
+ * before it is read).
+ * Errors: as dla_forward; DLA_E_WORKSPACE when the problem needs more than
+ * DLA_NOALLOC_SCRATCH_BYTES of workspace (dla_plan_check's ws_fwd), in
+ * which case nothing is enqueued.
+ */
+#define DLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dla_forward_noalloc(const dla_desc* desc, const dla_shape* shape, const void* q, const void* k,
+                        const void* v, void* o, float* lse, void* stream);
 
 /*
  * Backward pass: gradients of sum(dout * o) with respect to q, k and v, where

@@ -3,6 +3,8 @@
 // enqueues nothing.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dla_kernels.h"
 
 namespace dla {
@@ -150,6 +152,67 @@ extern "C" int dla_forward(const dla_desc* desc, const dla_shape* shape, const v
   int rc = make_plan(desc, shape, &pl);
   if (rc) return rc;
   return forward_impl(pl, q, k, v, nullptr, nullptr, o, lse, ws, ws_bytes, stream);
+}
+
+// ---- The forward for callers that cannot allocate --------------------------
+//
+// A file-scope device array stands in for the caller's workspace.  Each GPU
+// holds its own copy (at its own address) from the moment the library's code
+// is loaded on it until the process ends.  Host code never passes the
+// array's name to a kernel or a copy: in host code that name is only a
+// stand-in; the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current and kept in `g_scratch_ptr`.
+namespace dla {
+constexpr size_t kScratchBytes = DLA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+}  // namespace dla
+
+static __device__ __align__(256) unsigned char scratch[dla::kScratchBytes];
+
+namespace dla {
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLA_E_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(DLA_E_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLA_OK;
+}
+}  // namespace
+}  // namespace dla
+
+extern "C" int dla_forward_noalloc(const dla_desc* desc, const dla_shape* shape, const void* q,
+                                   const void* k, const void* v, void* o, float* lse,
+                                   void* stream) {
+  clear_error();
+  Plan pl;
+  int rc = make_plan(desc, shape, &pl);
+  if (rc) return rc;
+  if (pl.ws_fwd > kScratchBytes)
+    return fail(DLA_E_WORKSPACE,
+                "dla_forward_noalloc: this problem needs %zu bytes of workspace, more than the %zu "
+                "bytes of the library's static scratch; call dla_forward with a workspace",
+                pl.ws_fwd, kScratchBytes);
+  if (pl.empty) return DLA_OK;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  // The partial results are written before they are read (every row a
+  // pattern keeps is written by its attention pass; the merge reads only
+  // those rows), so nothing in the scratch needs clearing between calls.
+  return forward_impl(pl, q, k, v, nullptr, nullptr, o, lse, ws, kScratchBytes, stream);
 }
 
 extern "C" int dla_forward_varlen(const dla_desc* desc, const dla_shape* shape,

@@ -29,7 +29,8 @@ EXPORTS = ("dla_plan_check", "dla_forward", "dla_backward", "dla_row_map", "dla_
            "dla_backward_shard", "dla_shard_finish", "dla_forward_varlen", "dla_backward_varlen",
            "dla_pair_count_varlen", "dla_blas_create", "dla_blas_destroy", "dla_layer_plan_check",
            "dla_layer_forward", "dla_layer_backward", "dla_quantize_fp8", "dla_forward_fp8kv",
-           "dla_timing_enable", "dla_timing_collect", "dla_strerror", "dla_last_error")
+           "dla_forward_noalloc", "dla_timing_enable", "dla_timing_collect", "dla_strerror",
+           "dla_last_error")
 
 
 class DlaError(RuntimeError):
@@ -73,6 +74,7 @@ def lib():
     pd, ps = ctypes.POINTER(Desc), ctypes.POINTER(Shape)
     L.dla_plan_check.argtypes = [pd, ps, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     L.dla_forward.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dla_forward_noalloc.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp]
     L.dla_backward.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dla_row_map.argtypes = [pd, i64, i32, i32, vp, vp]
     L.dla_pair_count.argtypes = [pd, ps, ctypes.POINTER(i64)]
@@ -111,7 +113,7 @@ def lib():
                  "dla_forward_shard", "dla_backward_shard", "dla_shard_finish",
                  "dla_forward_varlen", "dla_backward_varlen", "dla_pair_count_varlen",
                  "dla_blas_create", "dla_blas_destroy", "dla_layer_plan_check", "dla_layer_forward",
-                 "dla_layer_backward", "dla_quantize_fp8", "dla_forward_fp8kv"):
+                 "dla_layer_backward", "dla_quantize_fp8", "dla_forward_fp8kv", "dla_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -230,6 +232,32 @@ def forward(q, k, v, patterns, causal=True, scale=None, out=None, lse=None, work
     _check(lib().dla_forward(ctypes.byref(desc), ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
                              v.data_ptr(), o.data_ptr(), lse_t.data_ptr(), workspace.data_ptr(),
                              workspace.numel(), _stream(stream, q.device)))
+    return o, lse_t
+
+
+# Bytes of the library's static scratch that dla_forward_noalloc uses as its workspace.
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(q, k, v, patterns, causal=True, scale=None, out=None, lse=None, stream=None):
+    """dla_forward_noalloc: the forward with the library's static scratch as
+    its workspace (no workspace argument, nothing allocated by the library).
+    The outputs are still the caller's: pass out/lse to allocate nothing at
+    all.  Raises DlaError(DLA_E_WORKSPACE) for problems whose workspace
+    exceeds NOALLOC_SCRATCH_BYTES.  Calls that overlap on one GPU race."""
+    import torch
+    scale = default_scale(q.shape[-1]) if scale is None else scale
+    _same_layout(q, k, v)
+    shape = _shape_of(q)
+    desc = make_desc(patterns, causal, scale)
+    B, N, H, _ = q.shape
+    o = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if out is None else out
+    _same_layout(q, o)
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_lse(lse_t, q)
+    _check(lib().dla_forward_noalloc(ctypes.byref(desc), ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                                     _stream(stream, q.device)))
     return o, lse_t
 
 
