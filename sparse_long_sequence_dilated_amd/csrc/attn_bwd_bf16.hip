@@ -39,6 +39,12 @@ constexpr int kBwdRows = 128;   // rows a unit owns (4 waves x 32)
 static_assert(kBwdRows == kBwdUnitRows, "the schedules and the kernel must agree on the unit size");
 constexpr int kBwdTile = 64;    // streamed rows per LDS tile
 constexpr int kBwdStages = 4;   // LDS ring depth (tiles in flight: 2)
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left alone
+// (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8); OR-ing in n < 16
+// allows n outstanding vector-memory operations.  Issued through the
+// builtin, not inline asm, so that the compiler's own wait insertion sees
+// it and accounts for every vector-memory operation it has placed.
+constexpr int kVmcnt0 = 0x0F70;
 
 struct __align__(16) BwdStage {
   uint4 a[kBwdTile * 8];   // Q (key units) or K (query units): 64 rows x 128 B
@@ -70,6 +76,7 @@ template <bool kKV, bool kWin>
 __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, int p, int b, int h,
                                          int64_t seg, int tile) {
   constexpr int kIns = kKV ? 5 : 4;  // DMA instructions per tile and wave
+  static_assert(2 * kIns < 16, "the waits encode vmcnt in 4 bits");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -416,12 +423,11 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
                        const BwdStage* __restrict__ sn, BwdStage* __restrict__ si) __attribute__((always_inline)) {
     if (kKV) DLA_BWD_PHASE(2 * j, 0, sp, sc, sc, sx, px, sx, px, pwx, swx, pwy, swy);
     else DLA_BWD_PHASE(2 * j, 0, sp, sc, sc, sx, px, sy, py, pwx, swx, pwy, swy);
-    if (j + 2 < nt) {
-      if (kKV) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    if (j + 2 < nt)
+      __builtin_amdgcn_s_waitcnt(kVmcnt0 | kIns);   // tile j+2's loads may stay in flight
+    else
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (j + 3 < nt) issue_tile(j + 3, si);
@@ -436,15 +442,13 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   issue_tile(0, &ring[0]);
   if (nt > 1) issue_tile(1, &ring[1]);
   if (nt > 2) issue_tile(2, &ring[2]);
-  if (nt > 2) {
-    if (kKV) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  } else if (nt > 1) {
-    if (kKV) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
+  if (nt > 2)
+    __builtin_amdgcn_s_waitcnt(kVmcnt0 | (2 * kIns));   // tiles 1 and 2 may stay in flight
+  else if (nt > 1)
+    __builtin_amdgcn_s_waitcnt(kVmcnt0 | kIns);
+  else
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   stage_sd(&ring[0], 0, sx, px);
@@ -456,7 +460,6 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   }
 #undef DLA_BWD_PHASE
 #undef DLA_DEAD
-  (void)kIns;
 
   // ---- epilogue: each wave's 32 owned rows go through LDS (chunk c of row i
   // at c ^ (i & 15), 256 B per row and tensor), so that every global store
