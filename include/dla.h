@@ -41,10 +41,11 @@
  *     pool of reusable events, behind a mutex), the thread-local error
  *     text, and dla_forward_noalloc's static device scratch (part of the
  *     library's code object, with its per-device addresses).  The
- *     exceptions are the attention layer's calls:
- *     dla_blas_create makes a hipBLASLt handle (its own host and device
- *     state), and each layer call creates and destroys hipBLASLt's small
- *     host-side descriptors.  Work is enqueued on `stream` (a hipStream_t;
+ *     exceptions are the attention layer's calls: dla_blas_create makes a
+ *     hipBLASLt handle (its own host and device state), and the handle
+ *     keeps, per product shape, the hipBLASLt descriptors and the algorithm
+ *     chosen on the first call with that shape (host memory, freed by
+ *     dla_blas_destroy).  Work is enqueued on `stream` (a hipStream_t;
  *     NULL is the null stream) and returns before it runs.
  *   - Descriptors are caller-owned host memory read only during the call.
  *   - Return value: DLA_OK or a negative DLA_E_* code.  All validation runs on
@@ -358,8 +359,11 @@ int dla_shard_finish(const dla_desc* desc, const dla_shape* shape, const dla_sha
  * (dla_blas_create); the attention is dla_forward / dla_backward.
  */
 
-/* Create / destroy the hipBLASLt handle the layer calls use (the only calls
- * that allocate: hipBLASLt's own host and device state). */
+/* Create / destroy the handle the layer calls use (the only calls that
+ * allocate: hipBLASLt's own host and device state, plus a per-shape cache
+ * of hipBLASLt descriptors and chosen algorithms, filled on the first call
+ * with each product shape and guarded by a mutex, so one handle may serve
+ * several threads).  The handle is opaque; pass it to the layer calls. */
 int dla_blas_create(void** handle);
 int dla_blas_destroy(void* handle);
 

@@ -13,6 +13,10 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <new>
+#include <tuple>
 
 #include "dla_device.h"
 
@@ -42,36 +46,63 @@ struct Batch {
   int64_t sa = 0, sb = 0, sc = 0;
 };
 
-// Row-major C = op(A) op(B) + beta C, A and B bf16, C bf16 or fp32, fp32
-// accumulation.  A is [M, K] (or [K, M] with ta), B is [K, N] (or [N, K]),
-// C is [M, N]; lda, ldb, ldc are their row-major leading dimensions.
-int gemm_rm(hipblasLtHandle_t h, hipStream_t st, void* ws, size_t ws_bytes, bool ta, bool tb,
-            int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-            int64_t ldb, void* C, int64_t ldc, hipDataType ctype, float beta,
-            const Batch& bt = Batch{}) {
-  int rc = DLA_OK;
+// The handle behind dla_blas_create: hipBLASLt's handle plus, per product
+// shape, the matmul and layout descriptors and the algorithm its heuristic
+// chose, made on the first call with that shape and reused afterwards.
+struct GemmKey {
+  bool ta, tb;
+  int64_t M, N, K, lda, ldb, ldc;
+  int ctype;
+  int count;
+  int64_t sa, sb, sc;
+  uint64_t ws;
+  bool operator<(const GemmKey& o) const {
+    return std::tie(ta, tb, M, N, K, lda, ldb, ldc, ctype, count, sa, sb, sc, ws) <
+           std::tie(o.ta, o.tb, o.M, o.N, o.K, o.lda, o.ldb, o.ldc, o.ctype, o.count, o.sa, o.sb, o.sc, o.ws);
+  }
+};
+struct GemmPlan {
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+};
+void destroy_plan(GemmPlan& g) {
+  if (g.lc) hipblasLtMatrixLayoutDestroy(g.lc);
+  if (g.lb) hipblasLtMatrixLayoutDestroy(g.lb);
+  if (g.la) hipblasLtMatrixLayoutDestroy(g.la);
+  if (g.desc) hipblasLtMatmulDescDestroy(g.desc);
+  g = GemmPlan{};
+}
+struct Blas {
+  hipblasLtHandle_t h = nullptr;
+  std::mutex mu;                      // guards `plans` (calls may come from several threads)
+  std::map<GemmKey, GemmPlan> plans;
+};
+
+// Descriptors and algorithm of one product shape; DLA_OK or an error code.
+// Row-major C[M, N] is issued as the column-major C^T = op(B)^T op(A)^T.
+int make_gemm_plan(hipblasLtHandle_t h, const GemmKey& k, GemmPlan* out) {
+  int rc = DLA_OK;
+  GemmPlan g;
   hipblasLtMatmulPreference_t pref = nullptr;
   hipblasLtMatmulHeuristicResult_t heur{};
   int found = 0;
-  const float alpha = 1.f;
-  // column-major operands: first = B (as op(B)^T), second = A (as op(A)^T)
-  const hipblasOperation_t op1 = tb ? HIPBLAS_OP_T : HIPBLAS_OP_N;
-  const hipblasOperation_t op2 = ta ? HIPBLAS_OP_T : HIPBLAS_OP_N;
-  const uint64_t wsb = ws_bytes;
-  DLA_BLAS(hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F));
-  DLA_BLAS(hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &op1, sizeof(op1)));
-  DLA_BLAS(hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &op2, sizeof(op2)));
-  DLA_BLAS(hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, tb ? K : N, tb ? N : K, ldb));
-  DLA_BLAS(hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, ta ? M : K, ta ? K : M, lda));
-  DLA_BLAS(hipblasLtMatrixLayoutCreate(&lc, ctype, N, M, ldc));
-  if (bt.count > 1) {
-    const hipblasLtMatrixLayout_t lay[3] = {la, lb, lc};
-    const int64_t stride[3] = {bt.sb, bt.sa, bt.sc};
+  const hipblasOperation_t op1 = k.tb ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+  const hipblasOperation_t op2 = k.ta ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+  const hipDataType ctype = (hipDataType)k.ctype;
+  const uint64_t wsb = k.ws;
+  DLA_BLAS(hipblasLtMatmulDescCreate(&g.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F));
+  DLA_BLAS(hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &op1, sizeof(op1)));
+  DLA_BLAS(hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &op2, sizeof(op2)));
+  DLA_BLAS(hipblasLtMatrixLayoutCreate(&g.la, HIP_R_16BF, k.tb ? k.K : k.N, k.tb ? k.N : k.K, k.ldb));
+  DLA_BLAS(hipblasLtMatrixLayoutCreate(&g.lb, HIP_R_16BF, k.ta ? k.M : k.K, k.ta ? k.K : k.M, k.lda));
+  DLA_BLAS(hipblasLtMatrixLayoutCreate(&g.lc, ctype, k.N, k.M, k.ldc));
+  if (k.count > 1) {
+    const hipblasLtMatrixLayout_t lay[3] = {g.la, g.lb, g.lc};
+    const int64_t stride[3] = {k.sb, k.sa, k.sc};
     for (int i = 0; i < 3; ++i) {
-      DLA_BLAS(hipblasLtMatrixLayoutSetAttribute(lay[i], HIPBLASLT_MATRIX_LAYOUT_BATCH_COUNT, &bt.count,
-                                                 sizeof(bt.count)));
+      DLA_BLAS(hipblasLtMatrixLayoutSetAttribute(lay[i], HIPBLASLT_MATRIX_LAYOUT_BATCH_COUNT, &k.count,
+                                                 sizeof(k.count)));
       DLA_BLAS(hipblasLtMatrixLayoutSetAttribute(lay[i], HIPBLASLT_MATRIX_LAYOUT_STRIDED_BATCH_OFFSET,
                                                  &stride[i], sizeof(stride[i])));
     }
@@ -79,20 +110,47 @@ int gemm_rm(hipblasLtHandle_t h, hipStream_t st, void* ws, size_t ws_bytes, bool
   DLA_BLAS(hipblasLtMatmulPreferenceCreate(&pref));
   DLA_BLAS(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
                                                  &wsb, sizeof(wsb)));
-  DLA_BLAS(hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, 1, &heur, &found));
+  DLA_BLAS(hipblasLtMatmulAlgoGetHeuristic(h, g.desc, g.la, g.lb, g.lc, g.lc, pref, 1, &heur, &found));
   if (found < 1) {
     rc = fail(DLA_E_UNSUPPORTED, "hipBLASLt has no algorithm for a %lldx%lldx%lld product",
-              (long long)M, (long long)N, (long long)K);
+              (long long)k.M, (long long)k.N, (long long)k.K);
     goto done;
   }
-  DLA_BLAS(hipblasLtMatmul(h, desc, &alpha, B, la, A, lb, &beta, C, lc, C, lc, &heur.algo, ws, ws_bytes,
-                           st));
+  g.algo = heur.algo;
 done:
   if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (lc) hipblasLtMatrixLayoutDestroy(lc);
-  if (lb) hipblasLtMatrixLayoutDestroy(lb);
-  if (la) hipblasLtMatrixLayoutDestroy(la);
-  if (desc) hipblasLtMatmulDescDestroy(desc);
+  if (rc == DLA_OK) *out = g;
+  else destroy_plan(g);
+  return rc;
+}
+
+// Row-major C = op(A) op(B) + beta C, A and B bf16, C bf16 or fp32, fp32
+// accumulation.  A is [M, K] (or [K, M] with ta), B is [K, N] (or [N, K]),
+// C is [M, N]; lda, ldb, ldc are their row-major leading dimensions.
+int gemm_rm(Blas* bl, hipStream_t st, void* ws, size_t ws_bytes, bool ta, bool tb,
+            int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+            int64_t ldb, void* C, int64_t ldc, hipDataType ctype, float beta,
+            const Batch& bt = Batch{}) {
+  int rc = DLA_OK;
+  const GemmKey key{ta, tb, M, N, K, lda, ldb, ldc, (int)ctype, bt.count,
+                    bt.count > 1 ? bt.sa : 0, bt.count > 1 ? bt.sb : 0, bt.count > 1 ? bt.sc : 0,
+                    (uint64_t)ws_bytes};
+  GemmPlan g;
+  {
+    std::lock_guard<std::mutex> lk(bl->mu);
+    auto it = bl->plans.find(key);
+    if (it == bl->plans.end()) {
+      if ((rc = make_gemm_plan(bl->h, key, &g))) return rc;
+      bl->plans.emplace(key, g);
+    } else {
+      g = it->second;
+    }
+  }
+  const float alpha = 1.f;
+  // column-major operands: first = B (as op(B)^T), second = A (as op(A)^T)
+  DLA_BLAS(hipblasLtMatmul(bl->h, g.desc, &alpha, B, g.la, A, g.lb, &beta, C, g.lc, C, g.lc, &g.algo, ws,
+                           ws_bytes, st));
+done:
   return rc;
 }
 #undef DLA_BLAS
@@ -193,13 +251,23 @@ extern "C" int dla_blas_create(void** handle) {
   hipblasLtHandle_t h = nullptr;
   const hipblasStatus_t s = hipblasLtCreate(&h);
   if (s != HIPBLAS_STATUS_SUCCESS) return fail(DLA_E_HIP, "hipblasLtCreate failed with status %d", (int)s);
-  *handle = h;
+  Blas* bl = new (std::nothrow) Blas;
+  if (!bl) {
+    hipblasLtDestroy(h);
+    return fail(DLA_E_HIP, "out of host memory");
+  }
+  bl->h = h;
+  *handle = bl;
   return DLA_OK;
 }
 
 extern "C" int dla_blas_destroy(void* handle) {
   clear_error();
-  if (handle) hipblasLtDestroy((hipblasLtHandle_t)handle);
+  if (!handle) return DLA_OK;
+  Blas* bl = (Blas*)handle;
+  for (auto& kv : bl->plans) destroy_plan(kv.second);
+  hipblasLtDestroy(bl->h);
+  delete bl;
   return DLA_OK;
 }
 
@@ -223,7 +291,7 @@ extern "C" int dla_layer_forward(const dla_desc* desc, int64_t B, int64_t N, int
     return rc;
   if (!blas) return fail(DLA_E_INVALID, "blas handle is null");
   if (ws_bytes < need) return fail(DLA_E_WORKSPACE, "layer workspace needs %zu bytes, got %zu", need, ws_bytes);
-  hipblasLtHandle_t h = (hipblasLtHandle_t)blas;
+  Blas* h = (Blas*)blas;
   hipStream_t st = (hipStream_t)stream;
   const int64_t M = B * N, E = H * kD;
   char* gws = (char*)ws + (need - kGemmWs);
@@ -258,7 +326,7 @@ extern "C" int dla_layer_backward(const dla_desc* desc, int64_t B, int64_t N, in
     return rc;
   if (!blas) return fail(DLA_E_INVALID, "blas handle is null");
   if (ws_bytes < need) return fail(DLA_E_WORKSPACE, "layer workspace needs %zu bytes, got %zu", need, ws_bytes);
-  hipblasLtHandle_t h = (hipblasLtHandle_t)blas;
+  Blas* h = (Blas*)blas;
   hipStream_t st = (hipStream_t)stream;
   const int64_t M = B * N, E = H * kD;
   char* da = (char*)ws;                                         // dA [M, E] bf16

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -22,6 +23,29 @@ int fail(int code, const char* fmt, ...) {
 }
 
 void clear_error() { g_err[0] = 0; }
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("DLA_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+// One line per plan: sizes, patterns and the derived layout (DLA_LOG=1).
+static void log_plan(const Plan& p) {
+  char pats[kMaxP * 24] = "";
+  size_t n = 0;
+  for (int i = 0; i < p.P && n < sizeof(pats); ++i)
+    n += snprintf(pats + n, sizeof(pats) - n, "%s(%d,%d)%s", i ? "," : "", p.w[i], p.r[i],
+                  p.span[i] ? "*" : "");
+  fprintf(stderr,
+          "[dla] plan: B=%lld N=%lld H=%lld %s %s patterns %s primary=%d merge=%d finalize=%d "
+          "pairs=%lld ws_fwd=%zu ws_bwd=%zu%s\n",
+          (long long)p.B, (long long)p.N, (long long)p.H, p.dtype == DLA_BF16 ? "bf16" : "fp32",
+          p.causal ? "causal" : "non-causal", pats, p.prim, (int)p.need_combine, (int)p.need_finalize,
+          (long long)p.pairs, p.ws_fwd, p.ws_bwd, p.shard ? " (shard; * spans devices)" : "");
+}
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -199,6 +223,7 @@ int make_plan(const dla_desc* desc, const dla_shape* shape, Plan* plan, const dl
   ovf |= __builtin_mul_overflow(pairs, p.B, &pairs);
   if (ovf) return fail(DLA_E_UNSUPPORTED, "the number of attention pairs exceeds 2^63");
   p.pairs = pairs;
+  if (log_enabled()) log_plan(p);
   return DLA_OK;
 }
 
@@ -261,6 +286,9 @@ void make_schedule(const Plan& p, int tile_rows, Schedule* s) {
   s->nband = nb;
   s->upg = start;
   s->total = start * groups;
+  if (log_enabled())
+    fprintf(stderr, "[dla] schedule: %d-row units, %lld units in %lld group(s) of %lld, %d band(s)\n",
+            tile_rows, (long long)s->total, (long long)groups, (long long)s->upg, nb);
 }
 
 }  // namespace dla

@@ -96,6 +96,10 @@ void make_schedule(const Plan& plan, int tile_rows, Schedule* s);
 // class).
 uint32_t class_step(const Plan& plan);
 
+// True when the environment has DLA_LOG=1 (read once): the planner then
+// writes one line per plan and per schedule to stderr.
+bool log_enabled();
+
 // Record a formatted message for dla_last_error() and return `code`.
 int fail(int code, const char* fmt, ...);
 void clear_error();

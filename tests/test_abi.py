@@ -283,3 +283,25 @@ def test_backward_entry_points_reject_a_bad_lse_before_any_launch(bad):
             call()
         assert ei.value.code == dla.DLA_E_INVALID
         assert "lse" in str(ei.value)
+
+
+@pytest.mark.parametrize("env", ["1", None])
+def test_planner_log_lines_only_with_dla_log(env):
+    """DLA_LOG=1 makes the host planner print one line per plan to stderr;
+    without it the library prints nothing."""
+    code = ("from sparse_long_sequence_dilated_amd import dla\n"
+            "dla.plan_check(((2048, 1), (4096, 2)), True, 0.125, 2, 8192, 3)\n")
+    e = dict(os.environ)
+    e.pop("DLA_LOG", None)
+    if env is not None:
+        e["DLA_LOG"] = env
+    out = subprocess.run([os.sys.executable, "-c", code], cwd=ROOT, env=e, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    lines = [ln for ln in out.stderr.splitlines() if ln.startswith("[dla]")]
+    if env is None:
+        assert lines == []
+    else:
+        assert len(lines) == 1
+        assert "B=2 N=8192 H=3 bf16 causal patterns (2048,1),(4096,2)" in lines[0]
+        assert "primary=0" in lines[0] and "pairs=" in lines[0]
