@@ -9,23 +9,28 @@
 // inside each sparsified segment (gptget.net LongNet summary, section 方法论),
 // with rows gathered by the same strided address generator as the forward.
 //
-// One launch covers all patterns with two kinds of workgroups (4 waves each):
+// Two launches cover all patterns, one per kind of workgroup (4 waves each):
 //   * key units own 128 keys (32 per wave), stream the segment's query rows
 //     (Q, dO, and the (LSE, D) pairs) and accumulate dK^T = Q^T dS and
-//     dV^T = dO^T P in registers;
+//     dV^T = dO^T P in registers; they need 256 VGPRs, so two workgroups
+//     share a CU, with a 4-stage LDS ring (66 KB);
 //   * query units own 128 queries (32 per wave), stream key rows (K, V) and
-//     accumulate dQ^T = K^T dS^T.
+//     accumulate dQ^T = K^T dS^T; they fit in 168 VGPRs and a 3-stage ring
+//     (49.5 KB), so three workgroups share a CU.
 // The owned rows sit in registers as MFMA B operands; the streamed rows go
-// from HBM into a 4-stage LDS ring with buffer_load ... lds (one 64-row tile
-// per stage, three tiles ahead), in one u-swizzled row-major copy that serves
-// both the row-wise operand reads (ds_read_b128) and the transposed ones
-// (ds_read_b64_tr_b16) without bank conflicts.  S and dP come out of
-// v_mfma_f32_32x32x16_bf16 with the lane on the owned row, so P and dS feed
-// the next MFMA as B operands straight from registers.
+// from HBM into the LDS ring with buffer_load ... lds (one 64-row tile per
+// stage, refilled as soon as its last reader is past a barrier), in one
+// u-swizzled row-major copy that serves both the row-wise operand reads
+// (ds_read_b128) and the transposed ones (ds_read_b64_tr_b16) without bank
+// conflicts.  S and dP come out of v_mfma_f32_32x32x16_bf16 with the lane on
+// the owned row, so P and dS feed the next MFMA as B operands straight from
+// registers.
 //
-// Work runs on 32-row halves h of the streamed side in a three-stage software
-// pipeline: phase h issues the MFMAs of half h+1 (S, dP) and of half h-1 (the
-// gradient products) while the VALU computes P and dS of half h.
+// Work runs on 32-row halves h of the streamed side: phase h issues the
+// gradient products of half h-1, computes P and dS of half h on the VALU,
+// and issues S and dP of half h+1.  Key units interleave the first two by
+// hand; query units keep one S/dP set (the third workgroup per CU hides
+// their latencies instead).
 //
 // Per output row the epilogue counts the patterns that keep it: a row kept by
 // this pattern alone gets its rounded gradient directly, a row kept by several
@@ -38,7 +43,6 @@ namespace dla {
 constexpr int kBwdRows = 128;   // rows a unit owns (4 waves x 32)
 static_assert(kBwdRows == kBwdUnitRows, "the schedules and the kernel must agree on the unit size");
 constexpr int kBwdTile = 64;    // streamed rows per LDS tile
-constexpr int kBwdStages = 4;   // LDS ring depth (tiles in flight: 2)
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left alone
 // (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8); OR-ing in n < 16
 // allows n outstanding vector-memory operations.  Issued through the
@@ -71,12 +75,15 @@ __device__ __forceinline__ bf16x8 words_bf16(const uint32_t (&w)[8], int half) {
 
 // kKV: key unit (dK, dV) or query unit (dQ).  kWin: the launch covers a
 // window [qlo, qhi) of a segment's query rows (one sequence shard's queries
-// against a gathered segment); every result is then an fp32 partial.
-template <bool kKV, bool kWin>
+// against a gathered segment); every result is then an fp32 partial.  NS:
+// LDS ring depth (4: tiles j+2 and j+3 in flight while tile j+1 is read; 3:
+// tile j+2 only).
+template <bool kKV, bool kWin, int NS>
 __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, int p, int b, int h,
                                          int64_t seg, int tile) {
   constexpr int kIns = kKV ? 5 : 4;  // DMA instructions per tile and wave
-  static_assert(2 * kIns < 16, "the waits encode vmcnt in 4 bits");
+  static_assert((NS - 2) * kIns < 16, "the waits encode vmcnt in 4 bits");
+  static_assert(NS == 3 || NS == 4, "ring depth 3 or 4");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
@@ -391,7 +398,7 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   do {                                                                                           \
     const bool a_prev = active((hh) - 1), a_cur = active(hh), a_next = active((hh) + 1);        \
     const bool msk = need_mask(hh);                                                              \
-    if (!kKV && a_prev && a_cur && a_next && !msk) {                                             \
+    if (!kKV && NS == 4 && a_prev && a_cur && a_next && !msk) {                                 \
       fused_q(sg, 1 - (blk), sw_prv, ss, 1 - (blk), S_nxt, P_nxt, blk, S_cur, P_cur, pw_cur, sw_cur); \
     } else {                                                                                     \
       if (kKV && !kWin && a_prev && a_cur && !msk) {                                             \
@@ -415,34 +422,36 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   } while (0)
 
   // Ring step j: phase 2j reads tiles j-1 and j; then wait until tile j+1
-  // is in LDS (tile j+2 may stay in flight), synchronise, refill the stage of
-  // tile j-1 with tile j+3, and run phase 2j+1 on tiles j and j+1.  The
+  // is in LDS, synchronise, refill the stage of tile j-1 with tile
+  // j + NS - 1, and run phase 2j+1 on tiles j and j+1.  The
   // distinct restrict pointers tell the compiler that the DMA target is not
   // read after the refill, so it adds no waits of its own.
   auto ring_step = [&](int j, const BwdStage* __restrict__ sp, const BwdStage* __restrict__ sc,
                        const BwdStage* __restrict__ sn, BwdStage* __restrict__ si) __attribute__((always_inline)) {
-    if (kKV) DLA_BWD_PHASE(2 * j, 0, sp, sc, sc, sx, px, sx, px, pwx, swx, pwy, swy);
+    if (kKV || NS == 3) DLA_BWD_PHASE(2 * j, 0, sp, sc, sc, sx, px, sx, px, pwx, swx, pwy, swy);
     else DLA_BWD_PHASE(2 * j, 0, sp, sc, sc, sx, px, sy, py, pwx, swx, pwy, swy);
-    if (j + 2 < nt)
-      __builtin_amdgcn_s_waitcnt(kVmcnt0 | kIns);   // tile j+2's loads may stay in flight
+    // With a 4-stage ring tile j+2 (if it exists) may stay in flight; with 3
+    // stages tile j+1 is the newest one issued.
+    if (NS == 4 && j + 2 < nt)
+      __builtin_amdgcn_s_waitcnt(kVmcnt0 | kIns);
     else
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (j + 3 < nt) issue_tile(j + 3, si);
-    if (kKV) DLA_BWD_PHASE(2 * j + 1, 1, sc, sn, sc, sx, px, sx, px, pwy, swy, pwx, swx);
+    if (j + NS - 1 < nt) issue_tile(j + NS - 1, si);
+    if (kKV || NS == 3) DLA_BWD_PHASE(2 * j + 1, 1, sc, sn, sc, sx, px, sx, px, pwy, swy, pwx, swx);
     else DLA_BWD_PHASE(2 * j + 1, 1, sc, sn, sc, sy, py, sx, px, pwy, swy, pwx, swx);
   };
 
-  // Prologue: tiles 0..2 in flight, wait for tile 0, S/dP of half 0.  (In a
-  // query window, a key tile past every query streams nothing and writes
-  // zeros.)
+  // Prologue: tiles 0 .. NS-2 in flight, wait for tile 0, S/dP of half 0.
+  // (In a query window, a key tile past every query streams nothing and
+  // writes zeros.)
   if (!kWin || nt > 0) {
   issue_tile(0, &ring[0]);
   if (nt > 1) issue_tile(1, &ring[1]);
-  if (nt > 2) issue_tile(2, &ring[2]);
-  if (nt > 2)
+  if (NS == 4 && nt > 2) issue_tile(2, &ring[2]);
+  if (NS == 4 && nt > 2)
     __builtin_amdgcn_s_waitcnt(kVmcnt0 | (2 * kIns));   // tiles 1 and 2 may stay in flight
   else if (nt > 1)
     __builtin_amdgcn_s_waitcnt(kVmcnt0 | kIns);
@@ -454,9 +463,9 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   stage_sd(&ring[0], 0, sx, px);
 
   for (int j = 0; j < nt; ++j)
-    ring_step(j, &ring[(j + 3) & 3], &ring[j & 3], &ring[(j + 1) & 3], &ring[(j + 3) & 3]);
+    ring_step(j, &ring[(j + NS - 1) % NS], &ring[j % NS], &ring[(j + 1) % NS], &ring[(j + NS - 1) % NS]);
   // Drain: gradient products of the last half.
-  if (active(2 * nt - 1)) stage_grad(&ring[(nt - 1) & 3], 1, pwy, swy);
+  if (active(2 * nt - 1)) stage_grad(&ring[(nt - 1) % NS], 1, pwy, swy);
   }
 #undef DLA_BWD_PHASE
 #undef DLA_DEAD
@@ -514,38 +523,50 @@ __device__ __forceinline__ void bwd_unit(const AttnBwdArgs& a, BwdStage* ring, i
   }
 }
 
+// Key units (dK, dV): 4-stage ring, 256 VGPRs (two waves per SIMD: two
+// workgroups per CU).  The schedules hand out the highest tile index first,
+// which is the most work for a query tile; under a causal mask a key tile
+// has the most work at index 0, so key tiles are taken in reverse.  Units
+// that touch the same rows are spread over the launch (a burst of them
+// would contend for the same L2 and memory channels).
 template <bool kWin>
-__global__ __launch_bounds__(256, 2) void attn_bwd_bf16_kernel(const AttnBwdArgs a) {
-  __shared__ BwdStage ring[kBwdStages];
-  // Longest first: the schedules hand out the highest tile index first, which
-  // is the most work for a query tile; under a causal mask a key tile has the
-  // most work at index 0, so key tiles are taken in reverse.  Units that touch
-  // the same rows are spread over the launch (a burst of them would contend
-  // for the same L2 and memory channels).
-  const uint32_t u = blockIdx.x;
-  const bool kv = u < (uint32_t)a.sched_kv.total;
+__global__ __launch_bounds__(256, 2) void attn_bwd_kv_kernel(const AttnBwdArgs a) {
+  __shared__ BwdStage ring[4];
   int p, b, h, tile;
   int64_t seg;
-  if (!decode_unit(kv ? a.sched_kv : a.sched_q, kv ? u : u - (uint32_t)a.sched_kv.total, (int)a.H, a.nseg,
-                   p, b, h, seg, tile))
-    return;
-  if (kv) {
-    if (a.causal) tile = (a.L[p] + kBwdRows - 1) / kBwdRows - 1 - tile;
-    bwd_unit<true, kWin>(a, ring, p, b, h, seg, tile);
-  } else {
-    if (kWin) tile += a.qlo / kBwdRows;                // the window's query tiles
-    bwd_unit<false, kWin>(a, ring, p, b, h, seg, tile);
-  }
+  if (!decode_unit(a.sched_kv, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile)) return;
+  if (a.causal) tile = (a.L[p] + kBwdRows - 1) / kBwdRows - 1 - tile;
+  bwd_unit<true, kWin, 4>(a, ring, p, b, h, seg, tile);
+}
+
+// Query units (dQ): 3-stage ring (49.5 KB) and at most 168 VGPRs (three
+// waves per SIMD), so that three workgroups share a CU.  They run after the
+// key units, in a launch of their own.
+template <bool kWin>
+__global__ __launch_bounds__(256, 3) void attn_bwd_q_kernel(const AttnBwdArgs a) {
+  __shared__ BwdStage ring[3];
+  int p, b, h, tile;
+  int64_t seg;
+  if (!decode_unit(a.sched_q, blockIdx.x, (int)a.H, a.nseg, p, b, h, seg, tile)) return;
+  if (kWin) tile += a.qlo / kBwdRows;                // the window's query tiles
+  bwd_unit<false, kWin, 3>(a, ring, p, b, h, seg, tile);
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream) {
-  const int64_t total = a.sched_kv.total + a.sched_q.total;
-  if (total == 0) return hipSuccess;
+  if (a.sched_kv.total + a.sched_q.total == 0) return hipSuccess;
   TimedLaunch tl("attn_bwd", stream);
-  if (a.qhi > 0)
-    hipLaunchKernelGGL(attn_bwd_bf16_kernel<true>, dim3((unsigned)total), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_bwd_bf16_kernel<false>, dim3((unsigned)total), dim3(256), 0, stream, a);
+  if (a.sched_kv.total > 0) {
+    if (a.qhi > 0)
+      hipLaunchKernelGGL(attn_bwd_kv_kernel<true>, dim3((unsigned)a.sched_kv.total), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_bwd_kv_kernel<false>, dim3((unsigned)a.sched_kv.total), dim3(256), 0, stream, a);
+  }
+  if (a.sched_q.total > 0) {
+    if (a.qhi > 0)
+      hipLaunchKernelGGL(attn_bwd_q_kernel<true>, dim3((unsigned)a.sched_q.total), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_bwd_q_kernel<false>, dim3((unsigned)a.sched_q.total), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
