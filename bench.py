@@ -3,14 +3,15 @@
 
 A step is one pass of the whole operator path over one batch already
 resident in HBM: dla_forward (attention over all patterns + merge) then
-dla_backward (preprocess + one launch per pattern), the operator's share of
+dla_backward (preprocess, attention backward over all patterns, sum of
+the patterns' partial gradients), the operator's share of
 a training step.  Default workload: bf16, B=2, N=32768, H=12, D=64, causal,
 patterns w = 2048*2^i, r = 2^i for i = 0..4 (the 768-dim, 12-head model
 settings of the gptget.net LongNet summary, section 实验设计, at 32K tokens).
 
 Also reported, as extra fields of the same line:
   * forward-only throughput of every forward workload: fp32 N=2048 (B=1,
-    non-causal, on the vector ALUs, also against the fp32 peak), bf16
+    non-causal, on the fp32 matrix cores, also against the fp32 peak), bf16
     N=8192 (B=4), N=32768 (B=1) and N=1,048,576 (B=1);
   * `shard_forward`: one device's share when the 1M-token sequence is split
     over 8 devices (the last shard, whose segments of the three coarsest
@@ -23,10 +24,11 @@ Also reported, as extra fields of the same line:
   * `cold_cache` (the step, and each forward line): kernel time per step when
     512 MB are written between steps, so no input stays in the 256 MB
     last-level cache (`value` is the warm, back-to-back step);
-  * `roofline` of the kernel family that takes most of the timed region,
-    timed live with HIP events around its launches on the launch stream;
-  * `ms_per_step_no_events`: the same steps again with the launch timing
-    off, which shows what the HIP events cost;
+  * `roofline` of the kernel family that takes most of the step, timed live
+    with HIP events around its launches on the launch stream, in a second
+    timed pass of the same steps (`ms_per_step_events` is that pass's wall
+    time; `ms_per_step` and `value` come from the first pass, which records
+    no events);
   * `cpu_baseline`: the CPU oracle (float32, thread pool) on a bounded
     sample of the same workload, scaled to the full workload.
 
@@ -129,14 +131,21 @@ def traffic_for(family, launches_per_step):
 
 
 def time_steps(step, steps, warmup):
-    """Wall time per step over `steps` timed steps (after `warmup`), with each
-    library launch bracketed by HIP events on its stream; returns
-    (ms per step, {family: (launches, total ms)})."""
+    """Time `steps` steps after `warmup` untimed ones, twice: first with the
+    library's launch timing off (the wall time per step that is reported),
+    then again with each library launch bracketed by HIP events on its own
+    stream (per-family kernel times).  Returns
+    (ms per step, {family: (launches, total ms)}, ms per step with events)."""
     import torch
     from sparse_long_sequence_dilated_amd import dla
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
     # fill the library's event pool so the timed steps create no events
     dla.timing_enable(True)
     step()
@@ -154,21 +163,10 @@ def time_steps(step, steps, warmup):
     dla.timing_enable(False)
     fams = {}
     for fam in FAMILIES:
-        n, ms = dla.timing_collect(fam)
+        n, fms = dla.timing_collect(fam)
         if n:
-            fams[fam] = (n, ms)
-    return (t1 - t0) * 1e3 / steps, fams
-
-
-def time_steps_plain(step, steps):
-    """Wall time per step with the launch timing off (no events recorded)."""
-    import torch
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+            fams[fam] = (n, fms)
+    return ms, fams, (t1 - t0) * 1e3 / steps
 
 
 def cold_kernel_ms(step, steps, flush_bytes=512 << 20):
@@ -208,13 +206,13 @@ def forward_only(name, steps, warmup):
     def step():
         dla.forward(q, k, v, wl.patterns, wl.causal, wl.scale, out=o, lse=lse, workspace=ws)
 
-    ms, fams = time_steps(step, steps, warmup)
+    ms, fams, _ = time_steps(step, steps, warmup)
     pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
     tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
     out = {"workload": wl.describe(), "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "ms": ms,
            "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS}
     if wl.dtype == "f32":
-        # fp32 runs on the vector ALUs: its own peak is the one that bounds it
+        # fp32 runs on the fp32 matrix cores: their peak is the one that bounds it
         out["pct_fp32_peak"] = 100.0 * tflops / FP32_PEAK_TFLOPS
     for fam, (n, fms) in fams.items():
         out[f"{fam}_us_per_launch"] = 1e3 * fms / n
@@ -248,8 +246,8 @@ def fp8_forward(name, steps, warmup):
         dla.forward_fp8kv(q, k8, v8, ks, vs, wl.patterns, wl.causal, wl.scale, out=o, lse=lse,
                           workspace=ws)
 
-    ms, fams = time_steps(step, steps, warmup)
-    qms, _ = time_steps(lambda: dla.quantize_fp8(k), steps, warmup)
+    ms, fams, _ = time_steps(step, steps, warmup)
+    qms, _, _ = time_steps(lambda: dla.quantize_fp8(k), steps, warmup)
     pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
     tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
     out = {"workload": wl.describe() + ", keys and values FP8 E4M3 with per-head scales",
@@ -294,7 +292,7 @@ def shard_forward(name, devices, shard, steps, warmup):
         dla.forward_shard(q, k, v, wl.patterns, wl.N, start, ext_k, ext_v, wl.causal, wl.scale,
                           out=o, lse=lse, workspace=ws)
 
-    ms, fams = time_steps(step, steps, warmup)
+    ms, fams, _ = time_steps(step, steps, warmup)
     pairs = dla.pair_count_shard(wl.patterns, wl.causal, wl.B, N, wl.H, wl.N, start)
     tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
     out = {"workload": f"{wl.describe()}, split over {devices} devices, shard {shard} "
@@ -320,7 +318,7 @@ def shard_forward(name, devices, shard, steps, warmup):
                            wl.scale, dq=dq, dk=dk, dv=dv, workspace=wsb)
         dla.finish_shard(dk, dv, wl.patterns, wl.N, start, red_k, red_v, wsb, wl.causal, wl.scale)
 
-    bms, bfams = time_steps(bstep, steps, warmup)
+    bms, bfams, _ = time_steps(bstep, steps, warmup)
     btf = 14 * wl.D * pairs / (bms * 1e-3) / 1e12
     out["fwd_bwd"] = {"tokens_per_s": wl.B * N / (bms * 1e-3), "ms": bms, "useful_tflops": btf,
                       "pct_bf16_peak": 100.0 * btf / BF16_PEAK_TFLOPS}
@@ -410,7 +408,7 @@ def layer_bench(B, N, steps, warmup):
     out = {"workload": f"attention layer E={E} H={H} (random weights), bf16, B={B}, N={N}, "
                        f"causal, patterns {[list(p) for p in pats]}"}
     for name, fn, mult in (("forward", fstep, 1), ("fwd_bwd", bstep, 3)):
-        ms, fams = time_steps(fn, steps, warmup)
+        ms, fams, _ = time_steps(fn, steps, warmup)
         attn_ms = sum(t for _, t in fams.values()) / steps
         flops = mult * gemm_flops + (4 if mult == 1 else 14) * D * pairs
         out[name] = {"tokens_per_s": B * N / (ms * 1e-3), "ms": ms,
@@ -477,8 +475,7 @@ def main():
             dla.backward(q, k, v, o, lse, do, wl.patterns, wl.causal, wl.scale, dq=dq, dk=dk,
                          dv=dv, workspace=ws_bwd)
 
-    ms, fams = time_steps(step, args.steps, args.warmup)
-    ms_plain = time_steps_plain(step, args.steps)
+    ms, fams, ms_events = time_steps(step, args.steps, args.warmup)
     pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
     flops = (14 if wl.backward else 4) * wl.D * pairs
     tflops = flops / (ms * 1e-3) / 1e12
@@ -523,7 +520,7 @@ def main():
                    "patterns": [list(p) for p in wl.patterns], "causal": wl.causal,
                    "step": "dla_forward + dla_backward" if wl.backward else "dla_forward"},
         "useful_tflops": tflops, "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
-        "ms_per_step_no_events": ms_plain,
+        "ms_per_step_events": ms_events,
         "roofline": roofline, "kernels": kernels, "forward_only": extra, "cpu_baseline": cpu,
         "cold_cache": {"kernel_ms_per_step": cold, "tokens_per_s": wl.B * wl.N / (cold * 1e-3),
                        "note": "512 MB written between steps; kernel time only"},
