@@ -507,7 +507,7 @@ def main():
         extra.append(forward_only("C3", max(5, args.steps), args.warmup))
         extra.append(forward_only("C4", max(3, args.steps // 4), 1))
         extra.append(fp8_forward("C3", max(5, args.steps), args.warmup))
-        shard = shard_forward("C4", 8, 7, max(3, args.steps // 2), 1)
+        shard = shard_forward("C4", 8, 7, max(3, args.steps // 2), 3)
         layers = [layer_bench(16, 2048, max(5, args.steps // 2), 2),
                   layer_bench(1, 32768, max(5, args.steps // 2), 2)]
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
