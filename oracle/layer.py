@@ -26,17 +26,20 @@ def _split(qkv, H):
     return [qkv[..., j * E:(j + 1) * E].reshape(B, N, H, E // H) for j in range(3)]
 
 
-def layer_forward(x, w_qkv, w_o, H, patterns, causal, scale, workers=1):
-    """Y [B, N, E] and the saved activations (q, k, v, attn, lse) of the layer."""
+def layer_forward(x, w_qkv, w_o, H, patterns, causal, scale, workers=1, attn_dtype=np.float64):
+    """Y [B, N, E] and the saved activations (q, k, v, attn, lse) of the layer.
+    `attn_dtype` is the precision of the attention step (the projections
+    stay float64); float32 serves large checks of bf16 results."""
     x, w_qkv, w_o = (np.asarray(t, np.float64) for t in (x, w_qkv, w_o))
     B, N, E = x.shape
     q, k, v = _split(x @ w_qkv, H)
-    attn, lse = forward(q, k, v, patterns, causal, scale, workers=workers)
+    attn, lse = forward(q, k, v, patterns, causal, scale, dtype=attn_dtype, workers=workers)
+    attn, lse = np.asarray(attn, np.float64), np.asarray(lse, np.float64)
     y = attn.reshape(B, N, E) @ w_o
     return y, (q, k, v, attn, lse)
 
 
-def layer_backward(x, w_qkv, w_o, saved, dy, patterns, causal, scale, workers=1):
+def layer_backward(x, w_qkv, w_o, saved, dy, patterns, causal, scale, workers=1, attn_dtype=np.float64):
     """(dX, dW_qkv, dW_o) of sum(dY * Y) by the chain rule through the layer.
 
     Y = A W_o gives dA = dY W_o^T and dW_o = A^T dY (summed over batch and
@@ -50,7 +53,9 @@ def layer_backward(x, w_qkv, w_o, saved, dy, patterns, causal, scale, workers=1)
     dy2 = dy.reshape(B * N, E)
     dw_o = a2.T @ dy2
     da = (dy2 @ w_o.T).reshape(attn.shape)
-    dq, dk, dv = backward(q, k, v, attn, lse, da, patterns, causal, scale, workers=workers)
+    dq, dk, dv = backward(q, k, v, attn, lse, da, patterns, causal, scale, dtype=attn_dtype,
+                          workers=workers)
+    dq, dk, dv = (np.asarray(t, np.float64) for t in (dq, dk, dv))
     dp = np.concatenate([t.reshape(B * N, E) for t in (dq, dk, dv)], axis=1)
     dx = (dp @ w_qkv.T).reshape(B, N, E)
     dw_qkv = x.reshape(B * N, E).T @ dp
