@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from sparse_long_sequence_dilated_amd import dla, inputs
-from tests.gpu_util import TOL, check_fwd, normwise, to_device, to_host
+from tests.gpu_util import ORACLE_WORKERS, TOL, check_fwd, normwise, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -106,8 +106,11 @@ def test_forward_shards_match_whole_sequence_oracle(case):
     eo, el = check_fwd(to_host(o), to_host(lse), o_ref, lse_ref, "bf16")
 
 
-def test_forward_shard_c4_eight_way_last_shard_sampled_rows():
-    """C4 split over 8 devices: the last shard (patterns i = 7..9 span 2, 4, 8 devices)."""
+@pytest.fixture(scope="module")
+def c4_last_shard():
+    """C4 split over 8 devices, the last shard (patterns i = 7..9 span 2, 4 and
+    8 devices), run once into NaN-filled outputs: (q, k, v, o, lse) on the
+    host for the shard's rows."""
     import torch
     wl = inputs.WORKLOADS["C4"]
     total, G = wl.N, 8
@@ -121,18 +124,32 @@ def test_forward_shard_c4_eight_way_last_shard_sampled_rows():
             ext_k[p] = _gathered(tk, wl.patterns, p, N, total, g)
             ext_v[p] = _gathered(tv, wl.patterns, p, N, total, g)
     sl = slice(g * N, (g + 1) * N)
-    o, lse = dla.forward_shard(tq[:, sl], tk[:, sl], tv[:, sl], wl.patterns, total, g * N,
-                               ext_k, ext_v, True, wl.scale)
+    o = torch.full_like(tq[:, sl], float("nan"))
+    lse = torch.full((wl.B, wl.H, N), float("nan"), dtype=torch.float32, device="cuda")
+    dla.forward_shard(tq[:, sl], tk[:, sl], tv[:, sl], wl.patterns, total, g * N,
+                      ext_k, ext_v, True, wl.scale, out=o, lse=lse)
     torch.cuda.synchronize()
     del tq, tk, tv, ext_k, ext_v
-    rng = np.random.default_rng(11)
-    special = np.array([0, 1, 255, 256, N // 2, N - 2, N - 1])
-    for h in (0, 7, 11):
-        local = np.unique(np.concatenate([special, rng.integers(0, N, 41)]))
-        o_ref, l_ref = oracle.forward_rows(q, k, v, wl.patterns, True, wl.scale, 0, h, g * N + local)
-        idx = torch.from_numpy(local).cuda()
-        check_fwd(o[0, :, h][idx].float().cpu().numpy(), lse[0, h][idx].cpu().numpy(), o_ref, l_ref,
-                  "bf16", f"C4 shard {g}/{G} head {h}:")
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    out = q, k, v, to_host(o), to_host(lse)
+    del o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.parametrize("h", range(12))
+def test_forward_shard_c4_eight_way_last_shard_full(c4_last_shard, h):
+    """Every row of the last of 8 C4 shards against the whole-sequence
+    float32 oracle, one head at a time."""
+    wl = inputs.WORKLOADS["C4"]
+    N = wl.N // 8
+    q, k, v, o, lse = c4_last_shard
+    hs = slice(h, h + 1)
+    o_ref, lse_ref = oracle.forward(q[:, :, hs], k[:, :, hs], v[:, :, hs], wl.patterns, True, wl.scale,
+                                    dtype=np.float32, workers=ORACLE_WORKERS, heads=[h])
+    rows = slice(wl.N - N, wl.N)
+    check_fwd(o[:, :, h], lse[:, h], o_ref[:, rows, 0], lse_ref[:, 0, rows], "bf16",
+              f"C4 shard 7/8 head {h}:")
 
 
 BWD_CASES = [
