@@ -32,6 +32,9 @@ Also reported, as extra fields of the same line:
   * `cpu_baseline`: the CPU oracle (float32, thread pool) on a bounded
     sample of the same workload, scaled to the full workload.
 
+The extra lines time their steps in three passes and keep the median pass;
+the headline step is timed once, exactly `--steps` steps.
+
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 from __future__ import annotations
@@ -130,22 +133,27 @@ def traffic_for(family, launches_per_step):
     return rec["bytes_per_step"] / max(1, launches_per_step) if rec.get("per") == "step" else rec.get("bytes_per_launch")
 
 
-def time_steps(step, steps, warmup):
+def time_steps(step, steps, warmup, reps=1):
     """Time `steps` steps after `warmup` untimed ones, twice: first with the
     library's launch timing off (the wall time per step that is reported),
     then again with each library launch bracketed by HIP events on its own
-    stream (per-family kernel times).  Returns
+    stream (per-family kernel times).  With reps > 1 (the extra lines, not
+    the headline step) the first pass is repeated and its median kept, so
+    that one host stall does not stand for the whole line.  Returns
     (ms per step, {family: (launches, total ms)}, ms per step with events)."""
     import torch
     from sparse_long_sequence_dilated_amd import dla
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    passes = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        passes.append((time.perf_counter() - t0) * 1e3 / steps)
+    ms = sorted(passes)[len(passes) // 2]
     # fill the library's event pool so the timed steps create no events
     dla.timing_enable(True)
     step()
@@ -206,7 +214,7 @@ def forward_only(name, steps, warmup):
     def step():
         dla.forward(q, k, v, wl.patterns, wl.causal, wl.scale, out=o, lse=lse, workspace=ws)
 
-    ms, fams, _ = time_steps(step, steps, warmup)
+    ms, fams, _ = time_steps(step, steps, warmup, reps=3)
     pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
     tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
     out = {"workload": wl.describe(), "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "ms": ms,
@@ -246,8 +254,8 @@ def fp8_forward(name, steps, warmup):
         dla.forward_fp8kv(q, k8, v8, ks, vs, wl.patterns, wl.causal, wl.scale, out=o, lse=lse,
                           workspace=ws)
 
-    ms, fams, _ = time_steps(step, steps, warmup)
-    qms, _, _ = time_steps(lambda: dla.quantize_fp8(k), steps, warmup)
+    ms, fams, _ = time_steps(step, steps, warmup, reps=3)
+    qms, _, _ = time_steps(lambda: dla.quantize_fp8(k), steps, warmup, reps=3)
     pairs = dla.pair_count(wl.patterns, wl.causal, wl.B, wl.N, wl.H)
     tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
     out = {"workload": wl.describe() + ", keys and values FP8 E4M3 with per-head scales",
@@ -292,7 +300,7 @@ def shard_forward(name, devices, shard, steps, warmup):
         dla.forward_shard(q, k, v, wl.patterns, wl.N, start, ext_k, ext_v, wl.causal, wl.scale,
                           out=o, lse=lse, workspace=ws)
 
-    ms, fams, _ = time_steps(step, steps, warmup)
+    ms, fams, _ = time_steps(step, steps, warmup, reps=3)
     pairs = dla.pair_count_shard(wl.patterns, wl.causal, wl.B, N, wl.H, wl.N, start)
     tflops = 4 * wl.D * pairs / (ms * 1e-3) / 1e12
     out = {"workload": f"{wl.describe()}, split over {devices} devices, shard {shard} "
@@ -318,7 +326,7 @@ def shard_forward(name, devices, shard, steps, warmup):
                            wl.scale, dq=dq, dk=dk, dv=dv, workspace=wsb)
         dla.finish_shard(dk, dv, wl.patterns, wl.N, start, red_k, red_v, wsb, wl.causal, wl.scale)
 
-    bms, bfams, _ = time_steps(bstep, steps, warmup)
+    bms, bfams, _ = time_steps(bstep, steps, warmup, reps=3)
     btf = 14 * wl.D * pairs / (bms * 1e-3) / 1e12
     out["fwd_bwd"] = {"tokens_per_s": wl.B * N / (bms * 1e-3), "ms": bms, "useful_tflops": btf,
                       "pct_bf16_peak": 100.0 * btf / BF16_PEAK_TFLOPS}
@@ -408,7 +416,7 @@ def layer_bench(B, N, steps, warmup):
     out = {"workload": f"attention layer E={E} H={H} (random weights), bf16, B={B}, N={N}, "
                        f"causal, patterns {[list(p) for p in pats]}"}
     for name, fn, mult in (("forward", fstep, 1), ("fwd_bwd", bstep, 3)):
-        ms, fams, _ = time_steps(fn, steps, warmup)
+        ms, fams, _ = time_steps(fn, steps, warmup, reps=3)
         attn_ms = sum(t for _, t in fams.values()) / steps
         flops = mult * gemm_flops + (4 if mult == 1 else 14) * D * pairs
         out[name] = {"tokens_per_s": B * N / (ms * 1e-3), "ms": ms,

@@ -115,19 +115,13 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   const int nh = wave_active ? (wave_kend + 31) / 32 : 0;  // half tiles this wave computes
   const float c = kFp8 ? a.scale_log2 * a.k_scale[(int64_t)b * a.H + h] : a.scale_log2;
 
-  // Q as the B operand: lane (query li, group lg) holds d = 16*ks + 8*lg .. +8,
-  // pre-multiplied by c (scale * log2 e, times the key scale for 8-bit keys)
-  // and rounded to bf16 once, so that the MFMA yields scores in the log2
-  // domain and P = exp2(S - m) needs no multiply per element.
+  // Q as the B operand: lane (query li, group lg) holds d = 16*ks + 8*lg .. +8.
   bf16x8 qop[4];
   {
     const int row = qw0 + li;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 x = row < L ? *(const bf16x8*)(Qh + (int64_t)row * rstride + 16 * ks + 8 * lg) : bf16x8{};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qop[ks][i] = (__bf16)((float)x[i] * c);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      qop[ks] = row < L ? *(const bf16x8*)(Qh + (int64_t)row * rstride + 16 * ks + 8 * lg) : bf16x8{};
   }
 
   // ---- HBM -> LDS: wave w fills rows [8w, 8w+8) of a tile with one
@@ -206,16 +200,10 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   for (int db = 0; db < 2; ++db) tr_offsets(lane, db, vlo[db], vhi[db]);
 
   f32x16 oacc[2] = {f32x16{}, f32x16{}};  // O^T[db]
-  float m_run = 0.f;                      // running offset (log2 domain) of this lane's query
+  float m_run = -INFINITY;                // running offset (log2 domain) of this lane's query
   float l_run = 0.f;                      // this lane's half of the row sum
   float pend = 1.f;                       // O rescale factor owed before O's next update
   bool owed = false;                      // (wave-uniform) some lane's pend may differ from 1
-  // (wave-uniform) every lane's offset is 0: the scores need no subtraction
-  // before exp2.  A wave starts so when its first half tile's row maxima
-  // lie in [-64, 12] (P then stays below 2^12 per key until a later key
-  // exceeds them, which the row-sum check catches); the offset cancels
-  // between numerator and denominator, so 0 is as exact as any.
-  bool fast = false;
 
   // ---- building blocks --------------------------------------------------------
   // K operand of step ks of S_h = K_h Q^T (half tile h in block blk of its stage).
@@ -231,14 +219,13 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k2, qop[2], s, 0, 0, 0);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k3, qop[3], s, 0, 0, 0);
   };
-  // Four elements (e = 4g .. 4g+3) of P from scores already offset by the
-  // running offset: two packed bf16 words; the row-sum terms go to two
-  // accumulators.
-  auto p_chunk = [&](const f32x16& s, int g, uint32_t (&pw)[8], float& r0, float& r1) __attribute__((always_inline)) {
-    const float x0 = __builtin_amdgcn_exp2f(s[4 * g]);
-    const float x1 = __builtin_amdgcn_exp2f(s[4 * g + 1]);
-    const float x2 = __builtin_amdgcn_exp2f(s[4 * g + 2]);
-    const float x3 = __builtin_amdgcn_exp2f(s[4 * g + 3]);
+  // Four elements (e = 4g .. 4g+3) of P with offset m: two packed bf16 words;
+  // the row-sum terms go to two accumulators.
+  auto p_chunk = [&](const f32x16& s, float m, int g, uint32_t (&pw)[8], float& r0, float& r1) __attribute__((always_inline)) {
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g], c, -m));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 1], c, -m));
+    const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 2], c, -m));
+    const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 3], c, -m));
     pw[2 * g] = pack_bf16(x0, x1);
     pw[2 * g + 1] = pack_bf16(x2, x3);
     if (g == 0) {
@@ -266,50 +253,39 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   auto mfma_o1 = [&](const FwdStage* __restrict__ st, int blk, int db, int kl, const uint32_t (&pw)[8]) __attribute__((always_inline)) {
     mfma_o(read_v(st, blk, db, kl), db, kl, pw);
   };
-  // Subtract the running offset from the scores (only off the fast path).
-  auto offset_s = [&](f32x16& s) __attribute__((always_inline)) {
-    if (!fast) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] -= m_run;
-    }
-  };
-  // Accept P computed with the running offset, or redo it with the true
-  // maximum (s holds the scores minus the old offset; masked ones are -inf).
-  auto finish_p = [&](f32x16& s, float rs, uint32_t (&pw)[8]) __attribute__((always_inline)) {
+  // Accept P computed with the running offset, or redo it with the true maximum.
+  auto finish_p = [&](const f32x16& s, float rs, uint32_t (&pw)[8]) __attribute__((always_inline)) {
     if (__builtin_amdgcn_ballot_w64(!(rs <= kSumLimit)) != 0) {
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-      const float up = fmaxf(xhalf_max(mx), 0.f);   // the offset rises by this much
-      const float alpha = __builtin_amdgcn_exp2f(-up);
+      mx = xhalf_max(mx) * c;
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       pend *= alpha;
       owed = true;
       l_run *= alpha;
-      m_run += up;
-      fast = __builtin_amdgcn_ballot_w64(m_run != 0.f) == 0;
+      m_run = m_new;
       float r0 = 0.f, r1 = 0.f;
+      const float m = m_new == -INFINITY ? 0.f : m_new;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] -= up;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) p_chunk(s, g, pw, r0, r1);
+      for (int g = 0; g < 4; ++g) p_chunk(s, m, g, pw, r0, r1);
       rs = r0 + r1;
     }
     l_run += rs;
   };
-  // P of a wave's first half tile: O and l are zero, so the offset is set
-  // from the exact row maximum at once (no rescale is owed): 0 when every
-  // lane's maximum lies in [-64, 12] (the fast path), else the maximum.
-  auto first_p = [&](f32x16& s, uint32_t (&pw)[8]) __attribute__((always_inline)) {
+  // P of a wave's first half tile: the offset is still -inf and O and l are
+  // zero, so the exact row maximum is taken at once (no rescale is owed)
+  // instead of computing P with the running offset first.
+  auto first_p = [&](const f32x16& s, uint32_t (&pw)[8]) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-    mx = xhalf_max(mx);
-    fast = __builtin_amdgcn_ballot_w64(!(mx >= -64.f && mx <= 12.f)) == 0;
-    m_run = fast ? 0.f : (mx == -INFINITY ? 0.f : mx);
-    offset_s(s);
+    m_run = xhalf_max(mx) * c;
+    const float m = m_run == -INFINITY ? 0.f : m_run;
     float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) p_chunk(s, g, pw, r0, r1);
+    for (int g = 0; g < 4; ++g) p_chunk(s, m, g, pw, r0, r1);
     l_run = r0 + r1;
   };
   // Causal diagonal / ragged tail mask of half tile hh.  Element e of a lane
@@ -349,7 +325,6 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
   auto phase = [&](int hh, int blk, const FwdStage* __restrict__ so, const FwdStage* __restrict__ ss,
                    uint32_t (&pprev)[8], uint32_t (&pcur)[8]) __attribute__((always_inline)) {
     mask_s(hh, s);
-    if (hh > 0) offset_s(s);
     float r0 = 0.f, r1 = 0.f;
     bf16x8 k0, k1;
     if (hh > 0) {
@@ -366,7 +341,7 @@ __global__ __launch_bounds__(512, 4) void attn_fwd_bf16_kernel(const AttnFwdArgs
           k1 = read_k(ss, 1 - blk, 1);
         }
         mfma_o(vc, g & 1, g >> 1, pprev);
-        p_chunk(s, g, pcur, r0, r1);
+        p_chunk(s, m_run, g, pcur, r0, r1);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
